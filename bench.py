@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 prefill matmul path on one MI355X.
+
+Workload: the FFN of one prefill at M=2048 tokens (the headline shape: Q4_K
+weights, K=3584):
+  gate, up : K=3584,  N=18944, Q4_K, one shared FP8 activation quantisation
+  down     : K=18944, N=3584,  Q6_K, input SiLU(g)*u
+One step is one pass of the whole path over that batch: pack the three
+weights (dequantise, absmax, E4M3 encode; one host sync each), quantise the
+FFN input once for gate and up, run gate and up, quantise the down input,
+run down.  Inputs are synthetic (seeded), resident in HBM before timing.
+
+value = GEMM FLOPs of the step (3 x 2*M*N*K) / measured step time, TFLOP/s.
+roofline = the gate/up GEMM kernel (2*M*N*K per launch) timed with HIP
+events on its own stream during the timed steps, against the 5.0 PFLOP/s
+dense FP8 peak.  cpu_baseline = the CPU oracle on a bounded sample of the
+same workload (see --help).
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
+                  for f in ("gemm.hip", "rz_device.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate/up GEMM launch from the committed counter runs, or
+    None when they are absent or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x_ffn, gate_blocks, gate, m_rows=64):
+    """Time the oracle on a bounded sample: pack the gate weight, quantise the
+    FFN input, compute 64 output rows of the gate GEMM."""
+    import numpy as np
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(threads, 16))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads, user_api="blas")
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        limiter = None
+    from oracle import fp8_path
+    t0 = time.perf_counter()
+    w8, dq_w, _ = fp8_path.pack_weight(gate.qtype, gate_blocks, gate.n, gate.k)
+    t1 = time.perf_counter()
+    a8, _, dq_a = fp8_path.quant_act(x_ffn)
+    t2 = time.perf_counter()
+    rows = np.linspace(0, x_ffn.shape[0] - 1, m_rows).astype(np.int64)
+    fp8_path.gemm_rows(a8, w8, rows, dq_a, dq_w)
+    t3 = time.perf_counter()
+    if limiter is not None:
+        limiter.restore_original_limits()
+    flops = 2.0 * m_rows * gate.n * gate.k
+    total = t3 - t0
+    log(f"cpu oracle: pack {t1 - t0:.2f}s quant {t2 - t1:.2f}s gemm({m_rows} rows) {t3 - t2:.2f}s")
+    return {
+        "value": flops / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"oracle (numpy) on the gate GEMM of the same workload: pack the full "
+                   f"{gate.n}x{gate.k} Q4_K weight ({t1 - t0:.2f}s), quantise the full "
+                   f"{x_ffn.shape[0]}x{x_ffn.shape[1]} input ({t2 - t1:.2f}s), exact GEMM of "
+                   f"{m_rows} of {x_ffn.shape[0]} output rows ({t3 - t2:.2f}s); value = those "
+                   f"rows' 2*m*N*K FLOPs / total time; BLAS threads = cores"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}), flush=True)
+        log("bench.py: only --gpus 1 is supported (the path is measured on one GPU's shard)")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    rz.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    ffn, down = W.config_groups(3)
+    gate, up = ffn.gemms
+    dn = down.gemms[0]
+    M = ffn.m
+    log(f"setup: M={M} gate/up N={gate.n} K={gate.k} Q4_K, down N={dn.n} K={dn.k} Q6_K")
+    x_ffn_h = ffn.activation()
+    x_down_h = down.activation()
+    gate_blocks_h = W.weight_blocks(gate.qtype, gate.w_seed, gate.n, gate.k)
+    up_blocks_h = W.weight_blocks(up.qtype, up.w_seed, up.n, up.k)
+    down_blocks_h = W.weight_blocks(dn.qtype, dn.w_seed, dn.n, dn.k)
+
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x_ffn, x_down = to(x_ffn_h), to(x_down_h)
+    b_gate, b_up, b_down = to(gate_blocks_h), to(up_blocks_h), to(down_blocks_h)
+    u8, f32 = torch.uint8, torch.float32
+    w8 = {g.name: torch.empty((g.n, g.k), dtype=u8, device=dev) for g in (gate, up, dn)}
+    Mp = rz.rz_pad_m(M)
+    a8_ffn = torch.empty((Mp, ffn.k), dtype=u8, device=dev)
+    a8_down = torch.empty((Mp, down.k), dtype=u8, device=dev)
+    sc_ffn = torch.empty(4, dtype=f32, device=dev)
+    sc_down = torch.empty(4, dtype=f32, device=dev)
+    y = {g.name: torch.empty((M, g.n), dtype=f32, device=dev) for g in (gate, up, dn)}
+    ws = rz.workspace(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=f32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write done")
+        del src, dst
+
+    phases = ["pack_gate", "pack_up", "pack_down", "quant_ffn", "gemm_gate", "gemm_up",
+              "quant_down", "gemm_down"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        scales = {}
+        mark(0)
+        _, scales["gate"], _ = rz.rz_fp8_pack_weight(gate.qtype, b_gate, gate.n, gate.k, w8["gate"], ws, stream)
+        mark(1)
+        _, scales["up"], _ = rz.rz_fp8_pack_weight(up.qtype, b_up, up.n, up.k, w8["up"], ws, stream)
+        mark(2)
+        _, scales["down"], _ = rz.rz_fp8_pack_weight(dn.qtype, b_down, dn.n, dn.k, w8["down"], ws, stream)
+        mark(3)
+        rz.rz_fp8_quant_act(x_ffn, a8_ffn, sc_ffn, ws, stream)
+        mark(4)
+        rz.rz_fp8_gemm(a8_ffn, w8["gate"], M, sc_ffn, scales["gate"], y["gate"], stream)
+        mark(5)
+        rz.rz_fp8_gemm(a8_ffn, w8["up"], M, sc_ffn, scales["up"], y["up"], stream)
+        mark(6)
+        rz.rz_fp8_quant_act(x_down, a8_down, sc_down, ws, stream)
+        mark(7)
+        rz.rz_fp8_gemm(a8_down, w8["down"], M, sc_down, scales["down"], y["down"], stream)
+        mark(8)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    ph = {p: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3 for i, p in enumerate(phases)}
+    flop = {g.name: 2.0 * M * g.n * g.k for g in (gate, up, dn)}
+    step_flop = sum(flop.values())
+    value = step_flop / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = {n: flop[n] / (ph["gemm_" + n] * 1e-6) / 1e12 for n in flop}
+    gateup_us = 0.5 * (ph["gemm_gate"] + ph["gemm_up"])
+    achieved = flop["gate"] / (gateup_us * 1e-6) / 1e12
+    plan = rz.rz_fp8_gemm_plan(M, gate.n, gate.k)
+    log("phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in ph.items()))
+    log(f"gate/up GEMM {gateup_us:.1f} us = {achieved:.1f} TFLOP/s ({achieved / FP8_PEAK_TFLOPS:.1%} of peak), "
+        f"plan BNxBM={plan[0]}x{plan[1]} threads={plan[2]} wgs={plan[3]}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": ("FFN prefill, M=2048: gate+up K=3584 N=18944 Q4_K sharing one FP8 activation, "
+                         "down K=18944 N=3584 Q6_K; step = pack 3 weights + 2 activation quants + 3 GEMMs"),
+            "m": M, "gate_up": [gate.n, gate.k], "down": [dn.n, dn.k],
+        },
+        "roofline": {
+            "kernel": f"fp8_gemm_kernel<{plan[0]},{plan[1]}> (gate/up, M=2048 N=18944 K=3584)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(),
+        },
+        "phases_us": {k: round(v, 2) for k, v in ph.items()},
+        "gemm_tflops": {k: round(v, 2) for k, v in gemm_tflops.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(x_ffn_h, gate_blocks_h, gate)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

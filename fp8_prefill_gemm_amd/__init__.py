@@ -1,0 +1,218 @@
+"""Python binding of librz_fp8: the FP8 prefill matmul path on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``librz_fp8.so`` (built for gfx950 by ``fp8_prefill_gemm_amd.build``); torch
+tensors are used for device memory and the current HIP stream.  There is no
+fallback: if the library is missing, importing the binding's functions
+raises.
+
+The functions carry the names of the C entry points (include/rz_fp8.h) and
+take torch tensors instead of raw pointers; outputs that are not passed in
+are allocated on the input's device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+Q4_K = 12
+Q6_K = 14
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+
+_STATUS = {0: "RZ_OK", -1: "RZ_ERR_NULL", -2: "RZ_ERR_QTYPE", -3: "RZ_ERR_SHAPE",
+           -4: "RZ_ERR_ALIGN", -5: "RZ_ERR_HIP", -6: "RZ_ERR_VALUE"}
+
+
+class RzError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_vp, _u32, _u64, _i32, _f32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ctypes.c_float
+_SIGS = {
+    "rz_block_bytes": (ctypes.c_size_t, [_i32]),
+    "rz_weight_bytes": (ctypes.c_size_t, [_i32, _u32, _u32]),
+    "rz_pad_m": (_u32, [_u32]),
+    "rz_workspace_bytes": (ctypes.c_size_t, []),
+    "rz_fp8_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
+    "rz_fp8_quant_act": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp, _vp]),
+    "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp]),
+    "rz_dequant_f32": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
+    "rz_absmax_f32": (_i32, [_vp, _u64, _vp, _vp, _vp]),
+    "rz_e4m3_encode": (_i32, [_vp, _u64, _f32, _vp, _vp]),
+    "rz_fp8_scales": (_i32, [_vp, _u64, _vp, _vp, _vp]),
+    "rz_fp8_gemm_plan": (_i32, [_u32, _u32, _u32, _vp]),
+    "rz_status_string": (ctypes.c_char_p, [_i32]),
+    "rz_last_error_string": (ctypes.c_char_p, []),
+    "rz_version": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load librz_fp8.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is missing: build it with `python -m fp8_prefill_gemm_amd.build` "
+                "(hipcc, gfx950); there is no fallback implementation")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RzError(status, lib().rz_last_error_string().decode(errors="replace"))
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("rz_fp8 works on device (cuda/hip) tensors only")
+
+
+def workspace(device) -> "torch.Tensor":
+    """A fresh device workspace of rz_workspace_bytes() bytes."""
+    torch = _torch()
+    return torch.empty(lib().rz_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def rz_pad_m(m: int) -> int:
+    return int(lib().rz_pad_m(m))
+
+
+def rz_weight_bytes(qtype: int, n: int, k: int) -> int:
+    return int(lib().rz_weight_bytes(qtype, n, k))
+
+
+def rz_workspace_bytes() -> int:
+    return int(lib().rz_workspace_bytes())
+
+
+def rz_fp8_gemm_plan(m: int, n: int, k: int) -> tuple[int, int, int, int]:
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().rz_fp8_gemm_plan(m, n, k, ctypes.cast(out, ctypes.c_void_p)))
+    return tuple(out)
+
+
+# ------------------------------------------------------------- entry points
+
+def rz_fp8_pack_weight(qtype: int, blocks, n: int, k: int, w_fp8=None, ws=None, stream=None):
+    """-> (w_fp8 uint8 [n][k], w_scale float, w_absmax float).  Syncs the stream."""
+    torch = _torch()
+    _require_cuda(blocks, w_fp8, ws)
+    dev = blocks.device
+    if w_fp8 is None:
+        w_fp8 = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = workspace(dev)
+    scale = ctypes.c_float()
+    amax = ctypes.c_float()
+    _check(lib().rz_fp8_pack_weight(qtype, _ptr(blocks), n, k, _ptr(w_fp8), ctypes.addressof(scale),
+                                    ctypes.addressof(amax), _ptr(ws), _stream(stream, dev)))
+    return w_fp8, scale.value, amax.value
+
+
+def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
+    """x fp32 [m][k] -> (a_fp8 uint8 [pad_m(m)][k], act_scale float32[2] = {absmax, dq})."""
+    torch = _torch()
+    _require_cuda(x, a_fp8, act_scale, ws)
+    m, k = x.shape
+    dev = x.device
+    if a_fp8 is None:
+        a_fp8 = torch.empty((rz_pad_m(m), k), dtype=torch.uint8, device=dev)
+    if act_scale is None:
+        act_scale = torch.empty(4, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(dev)
+    _check(lib().rz_fp8_quant_act(_ptr(x), m, k, _ptr(a_fp8), _ptr(act_scale), _ptr(ws),
+                                  _stream(stream, dev)))
+    return a_fp8, act_scale
+
+
+def rz_fp8_gemm(a_fp8, w_fp8, m: int, act_scale, w_scale: float, y=None, stream=None):
+    """-> y fp32 [m][n] = dec(a)[:m] @ dec(w)^T * act_scale[1] * w_scale."""
+    torch = _torch()
+    _require_cuda(a_fp8, w_fp8, act_scale, y)
+    n, k = w_fp8.shape
+    dev = w_fp8.device
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    _check(lib().rz_fp8_gemm(_ptr(a_fp8), _ptr(w_fp8), m, n, k, _ptr(act_scale), float(w_scale),
+                             _ptr(y), _stream(stream, dev)))
+    return y
+
+
+def rz_dequant_f32(qtype: int, blocks, n: int, k: int, out=None, stream=None):
+    torch = _torch()
+    _require_cuda(blocks, out)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
+    _check(lib().rz_dequant_f32(qtype, _ptr(blocks), n, k, _ptr(out), _stream(stream, blocks.device)))
+    return out
+
+
+def rz_absmax_f32(x, out=None, ws=None, stream=None):
+    torch = _torch()
+    _require_cuda(x, out, ws)
+    if out is None:
+        out = torch.empty(4, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(x.device)
+    _check(lib().rz_absmax_f32(_ptr(x), x.numel(), _ptr(out), _ptr(ws), _stream(stream, x.device)))
+    return out
+
+
+def rz_e4m3_encode(x, scale: float, out=None, stream=None):
+    torch = _torch()
+    _require_cuda(x, out)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().rz_e4m3_encode(_ptr(x), x.numel(), float(scale), _ptr(out), _stream(stream, x.device)))
+    return out
+
+
+def rz_fp8_scales(absmax, q=None, dq=None, stream=None):
+    torch = _torch()
+    _require_cuda(absmax, q, dq)
+    if q is None:
+        q = torch.empty_like(absmax)
+    if dq is None:
+        dq = torch.empty_like(absmax)
+    _check(lib().rz_fp8_scales(_ptr(absmax), absmax.numel(), _ptr(q), _ptr(dq),
+                               _stream(stream, absmax.device)))
+    return q, dq

@@ -1,0 +1,190 @@
+// Activation quantisation and the element-wise diagnostics.
+//
+// Source: realizar 0.8.4 source pages cublas_prefill/gemm.rs,
+// cublas_prefill_fp8_gemm (device absmax over the m*k real elements, then a
+// device-scaled E4M3 conversion; no host synchronisation; M padded to 16),
+// and cublas_prefill/mod.rs, ABSMAX_REDUCE_PTX, F32_TO_E4M3_DEVICE_SCALED_PTX
+// and F32_TO_E4M3_SCALED_PTX.
+//
+// The pages reduce with a shared-memory tree and a global atomic max into a
+// word that must first be zeroed by a host-to-device copy.  Here the
+// reduction is two-pass and atomic-free: pass 1 writes one key per
+// workgroup (wave shuffles + LDS), pass 2 (the encoder) starts by reducing
+// those keys in every workgroup, so no zeroing and no extra launch is
+// needed, and workgroup 0 publishes {absmax, absmax'/448} for the GEMM.
+// HBM traffic: read x twice (4 + 4 bytes per element) and write 1 byte.
+#include "rz_device.h"
+#include "rz_internal.h"
+
+namespace rz {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Pass 1 over fp32 data: per-workgroup max key.  x is 16-byte aligned; the
+// last count % 4 elements are read one at a time by workgroup 0.
+__global__ __launch_bounds__(kThreads) void absmax_partial_kernel(const float* __restrict__ x,
+                                                                  uint64_t count,
+                                                                  uint32_t* __restrict__ partial) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const uint64_t n4 = count >> 2;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    uint32_t k0 = 0, k1 = 0;
+    uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    // two loads in flight per iteration
+    for (; i + stride < n4; i += 2 * stride) {
+        const float4 a = x4[i];
+        const float4 b = x4[i + stride];
+        uint32_t t;
+        t = abs_key(a.x); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.y); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.z); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.w); k0 = k0 > t ? k0 : t;
+        t = abs_key(b.x); k1 = k1 > t ? k1 : t;
+        t = abs_key(b.y); k1 = k1 > t ? k1 : t;
+        t = abs_key(b.z); k1 = k1 > t ? k1 : t;
+        t = abs_key(b.w); k1 = k1 > t ? k1 : t;
+    }
+    if (i < n4) {
+        const float4 a = x4[i];
+        uint32_t t;
+        t = abs_key(a.x); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.y); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.z); k0 = k0 > t ? k0 : t;
+        t = abs_key(a.w); k0 = k0 > t ? k0 : t;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (count & 3)) {
+        const uint32_t t = abs_key(x[(n4 << 2) + threadIdx.x]);
+        k0 = k0 > t ? k0 : t;
+    }
+    uint32_t key = block_max_u32<kThreads>(k0 > k1 ? k0 : k1, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = key;
+}
+
+// Pass 2 of the activation path.  count_real = m*k (a multiple of 256),
+// count_total = pad_m(m)*k; groups of 16 elements at or past count_real are
+// pad rows and are written as zero bytes.
+__global__ __launch_bounds__(kThreads) void act_encode_kernel(
+    const float* __restrict__ x, uint64_t count_real, uint64_t count_total,
+    const uint32_t* __restrict__ partial, int npartial, uint8_t* __restrict__ out,
+    float* __restrict__ act_scale) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        act_scale[0] = sc.a;
+        act_scale[1] = sc.dq;
+    }
+    const float q = sc.q;
+    const uint64_t groups = count_total >> 4;
+    const uint64_t real_groups = count_real >> 4;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    uint4* o16 = reinterpret_cast<uint4*>(out);
+    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += stride) {
+        if (g < real_groups) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 a = x4[4 * g + j];
+                v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+            }
+            uint32_t c[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] = e4m3_scaled(v[j], q);
+            o16[g] = pack16(c);
+        } else {
+            o16[g] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+// Final reduction for the absmax diagnostic: one workgroup.
+__global__ __launch_bounds__(kThreads) void absmax_final_kernel(const uint32_t* __restrict__ partial,
+                                                                int npartial, float* __restrict__ out) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const uint32_t key = reduce_partials<kThreads>(partial, npartial, red);
+    if (threadIdx.x == 0) out[0] = __uint_as_float(key);
+}
+
+// Host-scaled encode of `count` elements (16 per thread; scalar tail).
+__global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ x, uint64_t count,
+                                                          float q, uint8_t* __restrict__ out) {
+    const uint64_t groups = count >> 4;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    for (uint64_t g = tid; g < groups; g += stride) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = x4[4 * g + j];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+        uint32_t c[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = e4m3_scaled(v[j], q);
+        reinterpret_cast<uint4*>(out)[g] = pack16(c);
+    }
+    const uint64_t tail = count & 15;
+    if (tid < tail) {
+        const uint64_t i = (groups << 4) + tid;
+        out[i] = (uint8_t)e4m3_scaled(x[i], q);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void scales_kernel(const float* __restrict__ a, uint64_t count,
+                                                          float* __restrict__ q,
+                                                          float* __restrict__ dq) {
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < count; i += stride) {
+        const float v = a[i];
+        const float ap = (v == 0.0f) ? 1.0f : v;
+        q[i] = kFp8Max / ap;
+        dq[i] = ap / kFp8Max;
+    }
+}
+
+int grid_for(uint64_t work_items, int cap) {
+    uint64_t g = (work_items + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
+}
+
+// Partial workgroups for an absmax over `count` floats: about 8 float4 per
+// thread, at most kMaxPartials.
+int absmax_groups(uint64_t count) { return grid_for(((count >> 2) + 7) / 8, kMaxPartials); }
+
+}  // namespace
+
+hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,
+                            uint8_t* a_fp8, float* act_scale, uint8_t* ws, hipStream_t st) {
+    uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
+    const int g1 = absmax_groups(count_real);
+    absmax_partial_kernel<<<g1, kThreads, 0, st>>>(x, count_real, partial);
+    const int g2 = grid_for(count_total >> 4, 4096);
+    act_encode_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, partial, g1, a_fp8,
+                                               act_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax(const float* x, uint64_t count, float* out, uint8_t* ws, hipStream_t st) {
+    uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
+    const int g1 = absmax_groups(count);
+    absmax_partial_kernel<<<g1, kThreads, 0, st>>>(x, count, partial);
+    absmax_final_kernel<<<1, kThreads, 0, st>>>(partial, g1, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* out,
+                         hipStream_t st) {
+    encode_kernel<<<grid_for((count >> 4) + 1, 8192), kThreads, 0, st>>>(x, count, scale, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hipStream_t st) {
+    scales_kernel<<<grid_for(count, 4096), kThreads, 0, st>>>(a, count, q, dq);
+    return hipGetLastError();
+}
+
+}  // namespace rz

@@ -1,0 +1,233 @@
+// C ABI of librz_fp8 (declared in include/rz_fp8.h): argument validation,
+// device check and launch sequencing.  Validation runs before any HIP call,
+// so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/rz_fp8.h"
+#include "rz_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(RZ_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool qtype_ok(int q) { return q == RZ_Q4_K || q == RZ_Q6_K; }
+
+// The kernels are built for gfx950 only; refuse any other device up front
+// (checked once per device ordinal).
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 ok, -1 unsupported
+
+int check_device(const char* fn) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(RZ_ERR_HIP, "%s: device ordinal %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (g_dev_state[dev] < 0)
+            return fail(RZ_ERR_HIP, "%s: device %d is %s; this library is built for gfx950 only", fn,
+                        dev, prop.gcnArchName);
+    }
+    if (g_dev_state[dev] < 0) return fail(RZ_ERR_HIP, "%s: device %d is not gfx950", fn, dev);
+    return RZ_OK;
+}
+
+int check_k(const char* fn, uint32_t k) {
+    if (k == 0 || (k % 256u) != 0)
+        return fail(RZ_ERR_SHAPE, "%s: k=%u must be a positive multiple of 256", fn, k);
+    return RZ_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+size_t rz_block_bytes(int qtype) {
+    return qtype == RZ_Q4_K ? 144u : qtype == RZ_Q6_K ? 210u : 0u;
+}
+
+size_t rz_weight_bytes(int qtype, uint32_t n, uint32_t k) {
+    if (!qtype_ok(qtype) || k % 256u != 0) return 0;
+    return (size_t)n * (k / 256u) * rz_block_bytes(qtype);
+}
+
+uint32_t rz_pad_m(uint32_t m) { return (m + 15u) & ~15u; }
+
+size_t rz_workspace_bytes(void) { return rz::kWsBytes; }
+
+const char* rz_status_string(int status) {
+    switch (status) {
+        case RZ_OK: return "ok";
+        case RZ_ERR_NULL: return "null pointer";
+        case RZ_ERR_QTYPE: return "unsupported weight type";
+        case RZ_ERR_SHAPE: return "invalid shape";
+        case RZ_ERR_ALIGN: return "misaligned pointer";
+        case RZ_ERR_HIP: return "HIP error";
+        case RZ_ERR_VALUE: return "invalid value";
+        default: return "unknown status";
+    }
+}
+
+const char* rz_last_error_string(void) { return g_last_error.c_str(); }
+
+const char* rz_version(void) { return "rz_fp8 0.1.0 gfx950"; }
+
+int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
+                       float* w_scale_host, float* w_absmax_host, void* ws, void* stream) {
+    static const char* fn = "rz_fp8_pack_weight";
+    if (!blocks || !w_fp8 || !w_scale_host || !ws) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
+    if (int r = check_k(fn, k)) return r;
+    if (n == 0) return fail(RZ_ERR_SHAPE, "%s: n must be positive", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: n*k too large", fn);
+    if (!aligned16(blocks) || !aligned16(w_fp8) || !aligned16(ws))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipStream_t st = as_stream(stream);
+    const uint64_t nb = (uint64_t)n * (k / 256u);
+    hipError_t e = rz::launch_pack(qtype, static_cast<const uint8_t*>(blocks), nb, w_fp8,
+                                   static_cast<uint8_t*>(ws), st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    float sc[4];
+    e = hipMemcpyAsync(sc, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof sc,
+                       hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    *w_scale_host = sc[2];
+    if (w_absmax_host) *w_absmax_host = sc[0];
+    return RZ_OK;
+}
+
+int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, float* act_scale_dev,
+                     void* ws, void* stream) {
+    static const char* fn = "rz_fp8_quant_act";
+    // x and a_fp8 may be NULL when m == 0 (nothing is read or written there)
+    if ((m != 0 && (!x || !a_fp8)) || !act_scale_dev || !ws)
+        return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (int r = check_k(fn, k)) return r;
+    if ((uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || m > 0xFFFFFFF0u)
+        return fail(RZ_ERR_SHAPE, "%s: m*k too large", fn);
+    if ((m != 0 && (!aligned16(x) || !aligned16(a_fp8))) || !aligned16(ws) ||
+        ((uintptr_t)act_scale_dev & 3u))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8,
+                                        act_scale_dev, static_cast<uint8_t*>(ws), as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n, uint32_t k,
+                const float* act_scale_dev, float w_scale, float* y, void* stream) {
+    static const char* fn = "rz_fp8_gemm";
+    if (int r = check_k(fn, k)) return r;
+    if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
+    if (!a_fp8 || !w_fp8 || !act_scale_dev || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS || (uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS ||
+        (uint64_t)m * n > RZ_MAX_ELEMS || m > 0x7FFFFFF0u || n > 0x7FFFFFF0u)
+        return fail(RZ_ERR_SHAPE, "%s: operand too large", fn);
+    if (!aligned16(a_fp8) || !aligned16(w_fp8) || !aligned16(y) || ((uintptr_t)act_scale_dev & 3u))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (w_scale != w_scale || w_scale - w_scale != 0.0f)
+        return fail(RZ_ERR_VALUE, "%s: w_scale must be finite", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_gemm(a_fp8, w_fp8, m, n, k, act_scale_dev, w_scale, y, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out) {
+    static const char* fn = "rz_fp8_gemm_plan";
+    if (!cfg_out) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (int r = check_k(fn, k)) return r;
+    const rz::GemmPlan p = rz::plan_gemm(m, n, k);
+    cfg_out[0] = p.bn;
+    cfg_out[1] = p.bm;
+    cfg_out[2] = p.threads;
+    cfg_out[3] = (m == 0 || n == 0) ? 0 : p.workgroups;
+    return RZ_OK;
+}
+
+int rz_dequant_f32(int qtype, const void* blocks, uint32_t n, uint32_t k, float* out_dev,
+                   void* stream) {
+    static const char* fn = "rz_dequant_f32";
+    if (!blocks || !out_dev) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
+    if (int r = check_k(fn, k)) return r;
+    if (n == 0) return fail(RZ_ERR_SHAPE, "%s: n must be positive", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: n*k too large", fn);
+    if (!aligned16(blocks) || !aligned16(out_dev))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_dequant_f32(qtype, static_cast<const uint8_t*>(blocks),
+                                          (uint64_t)n * (k / 256u), out_dev, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_absmax_f32(const float* x, uint64_t count, float* out_dev, void* ws, void* stream) {
+    static const char* fn = "rz_absmax_f32";
+    if ((count != 0 && !x) || !out_dev || !ws) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (count > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: count too large", fn);
+    if ((count != 0 && !aligned16(x)) || !aligned16(ws) || ((uintptr_t)out_dev & 3u))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_absmax(x, count, out_dev, static_cast<uint8_t*>(ws), as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_e4m3_encode(const float* x, uint64_t count, float scale, uint8_t* out, void* stream) {
+    static const char* fn = "rz_e4m3_encode";
+    if (count == 0) return RZ_OK;
+    if (!x || !out) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (count > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: count too large", fn);
+    if (!aligned16(x) || !aligned16(out))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_encode(x, count, scale, out, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_fp8_scales(const float* absmax_dev, uint64_t count, float* q_out_dev, float* dq_out_dev,
+                  void* stream) {
+    static const char* fn = "rz_fp8_scales";
+    if (count == 0) return RZ_OK;
+    if (!absmax_dev || !q_out_dev || !dq_out_dev) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (count > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: count too large", fn);
+    if (((uintptr_t)absmax_dev | (uintptr_t)q_out_dev | (uintptr_t)dq_out_dev) & 3u)
+        return fail(RZ_ERR_ALIGN, "%s: pointers must be 4-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_scales(absmax_dev, count, q_out_dev, dq_out_dev, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+/*
+ * rz_fp8 — FP8 (E4M3) prefill matmul path for GGUF K-quant weights on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path (realizar 0.8.4 source pages, cublas_prefill/gemm.rs and
+ * cublas_prefill/mod.rs):
+ *   1. once per weight: Q4_K/Q6_K super-blocks -> fp32 -> per-tensor absmax
+ *      -> E4M3 bytes of RN(w * RN(448/absmax)) (absmax 0 treated as 1),
+ *      kept with the host scale RN(absmax/448)       [rz_fp8_pack_weight]
+ *   2. per distinct activation: device absmax and E4M3 conversion with no
+ *      host synchronisation, reused by every GEMM that reads the same input
+ *                                                     [rz_fp8_quant_act]
+ *   3. FP8 x FP8 GEMM with fp32 accumulation and an epilogue that multiplies
+ *      by (act_absmax/448) * (w_absmax/448), fp32 output  [rz_fp8_gemm]
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer named *_dev / device is device memory owned by the
+ *     caller; *_host is host memory owned by the caller.  The library keeps
+ *     no persistent device allocation of its own.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is ordered on it.  Only rz_fp8_pack_weight synchronises it.
+ *   - Arguments are validated before anything is launched.  Errors return a
+ *     negative rz_status and leave outputs untouched; nothing aborts.
+ *     rz_last_error_string() gives a message for the calling thread.
+ *   - Device pointers to tensors and to `ws` must be 16-byte aligned; pointers
+ *     to scalars (act_scale_dev, absmax/scale arrays) 4-byte aligned
+ *     (RZ_ERR_ALIGN otherwise).
+ *   - K (the reduction dimension) must be a positive multiple of 256, the
+ *     K-quant super-block length (RZ_ERR_SHAPE otherwise).
+ *   - `ws` is a caller-provided device workspace of rz_workspace_bytes()
+ *     bytes.  Calls that use the same `ws` must be ordered (same stream).
+ */
+#ifndef RZ_FP8_H
+#define RZ_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGML tensor type ids of the supported weight formats. */
+typedef enum { RZ_Q4_K = 12, RZ_Q6_K = 14 } rz_qtype;
+
+typedef enum {
+    RZ_OK = 0,
+    RZ_ERR_NULL = -1,   /* a required pointer is NULL */
+    RZ_ERR_QTYPE = -2,  /* weight type other than Q4_K / Q6_K */
+    RZ_ERR_SHAPE = -3,  /* k not a positive multiple of 256, n == 0, size limits */
+    RZ_ERR_ALIGN = -4,  /* a device pointer is not 16-byte aligned */
+    RZ_ERR_HIP = -5,    /* a HIP runtime call failed, or the device is not gfx950 */
+    RZ_ERR_VALUE = -6   /* a scalar argument is not finite where it must be */
+} rz_status;
+
+/* Largest accepted n*k (weights) and m*k (activations): 2^36 elements. */
+#define RZ_MAX_ELEMS ((uint64_t)1 << 36)
+
+/* Bytes per super-block of 256 weights: 144 (Q4_K, 0.5625 B/weight, as the
+ * gemm.rs page states) or 210 (Q6_K); 0 for any other type. */
+size_t rz_block_bytes(int qtype);
+
+/* Bytes of a [n][k] K-quant weight: n * (k/256) * rz_block_bytes(qtype);
+ * 0 if the type or k is invalid. */
+size_t rz_weight_bytes(int qtype, uint32_t n, uint32_t k);
+
+/* M rounded up to a multiple of 16 — the row count of the FP8 activation
+ * buffer (gemm.rs page, cublas_prefill_fp8_gemm: M is padded to 16). */
+uint32_t rz_pad_m(uint32_t m);
+
+/* Size in bytes of the device workspace `ws` (a constant, a few KB). */
+size_t rz_workspace_bytes(void);
+
+/*
+ * Pack one K-quant weight into FP8 E4M3 (gemm.rs page,
+ * get_or_cache_fp8_weight; mod.rs page, F32_TO_E4M3_SCALED_PTX and
+ * ABSMAX_REDUCE_PTX).
+ *
+ *   blocks        device, n*(k/256) super-blocks, row-major: row r of the
+ *                 weight is blocks r*(k/256) .. r*(k/256)+k/256-1
+ *   w_fp8         device out, uint8 [n][k] row-major E4M3 codes of
+ *                 RN(w * RN(448/a')), where a = max|w| (NaN ignored) and
+ *                 a' = a, or 1 when a == 0
+ *   w_scale_host  host out, RN(a'/448): the weight's dequantisation scale
+ *   w_absmax_host host out (may be NULL): a
+ *   ws            device workspace of rz_workspace_bytes()
+ * The dequantised fp32 weight is never materialised.  Synchronises `stream`
+ * once, to return the scale to the host.
+ */
+int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k,
+                       uint8_t* w_fp8, float* w_scale_host, float* w_absmax_host,
+                       void* ws, void* stream);
+
+/*
+ * Quantise an fp32 activation to FP8 on the device, with no host
+ * synchronisation (gemm.rs page, cublas_prefill_fp8_gemm steps 1-2; mod.rs
+ * page, F32_TO_E4M3_DEVICE_SCALED_PTX).
+ *
+ *   x             device, fp32 [m][k] row-major
+ *   a_fp8         device out, uint8 [rz_pad_m(m)][k]: rows < m hold the E4M3
+ *                 codes of RN(x * RN(448/a')), a = max|x| over the m*k real
+ *                 elements (NaN ignored); rows m..rz_pad_m(m)-1 are zero
+ *   act_scale_dev device out, float[2] = { a, RN(a'/448) }
+ * m == 0 is allowed (writes {0, RN(1/448)} and no codes; x and a_fp8 may
+ * then be NULL).  The outputs may
+ * be passed to any number of rz_fp8_gemm calls that read the same input.
+ */
+int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
+                     float* act_scale_dev, void* ws, void* stream);
+
+/*
+ * FP8 GEMM with fused dequantisation epilogue (gemm.rs page,
+ * cublas_prefill_fp8_gemm steps 3-4; mod.rs page, F16_TO_F32_ACT_SCALED_PTX).
+ *
+ *   y[i][j] = (sum_k dec(a_fp8[i][kk]) * dec(w_fp8[j][kk]))
+ *             * act_scale_dev[1] * w_scale          for i < m, j < n
+ *
+ *   a_fp8         device, uint8 [rz_pad_m(m)][k] from rz_fp8_quant_act
+ *   w_fp8         device, uint8 [n][k] from rz_fp8_pack_weight
+ *   act_scale_dev device, float[2] from rz_fp8_quant_act
+ *   w_scale       the host scale from rz_fp8_pack_weight
+ *   y             device out, fp32 [m][n] row-major (only rows < m written)
+ * Products are accumulated in fp32 on the matrix cores (no fp16 stage).
+ * m == 0 or n == 0 is a no-op (any pointer may then be NULL).
+ */
+int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
+                uint32_t k, const float* act_scale_dev, float w_scale, float* y,
+                void* stream);
+
+/* ---------------------------------------------------------------------
+ * Diagnostics: the individual steps, exposed so that each can be checked
+ * against the oracle.  Same conventions as above.
+ * --------------------------------------------------------------------- */
+
+/* Dequantise a K-quant weight to fp32 [n][k] row-major (gemm.rs page,
+ * launch_dequant_q4k / launch_dequant_q6k).  Each value is the correctly
+ * rounded fp32 of the format's exact value. */
+int rz_dequant_f32(int qtype, const void* blocks, uint32_t n, uint32_t k,
+                   float* out_dev, void* stream);
+
+/* out_dev[0] = max |x| over `count` fp32 values, NaN ignored, 0 when
+ * count == 0 (x may then be NULL) (mod.rs page, ABSMAX_REDUCE_PTX). */
+int rz_absmax_f32(const float* x, uint64_t count, float* out_dev, void* ws,
+                  void* stream);
+
+/* out[i] = E4M3 code of RN(x[i] * scale) for i < count (mod.rs page,
+ * F32_TO_E4M3_SCALED_PTX; with scale 1 the plain F32_TO_E4M3_PTX up to the
+ * sign of NaN, which the multiply makes positive).  count == 0 is a no-op. */
+int rz_e4m3_encode(const float* x, uint64_t count, float scale, uint8_t* out,
+                   void* stream);
+
+/* For each of `count` absmax values a: q_out = RN(448/a'), dq_out =
+ * RN(a'/448) with a' = a or 1 when a == 0 (mod.rs page,
+ * F32_TO_E4M3_DEVICE_SCALED_PTX; gemm.rs page, get_or_cache_fp8_weight).
+ * count == 0 is a no-op. */
+int rz_fp8_scales(const float* absmax_dev, uint64_t count, float* q_out_dev,
+                  float* dq_out_dev, void* stream);
+
+/* GEMM tile configuration rz_fp8_gemm would launch for this shape:
+ * writes {BN, BM, threads, workgroups} to cfg_out[4] (host). */
+int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out);
+
+const char* rz_status_string(int status);
+const char* rz_last_error_string(void);
+
+/* Library version, e.g. "rz_fp8 0.1.0 gfx950". */
+const char* rz_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RZ_FP8_H */

@@ -1,0 +1,146 @@
+"""C ABI contract of librz_fp8.so, checked without a GPU.
+
+The library must load, export every function include/rz_fp8.h declares, and
+reject bad arguments before any HIP call (so these run on a CPU-only host).
+The pointers used here are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_prefill_gemm_amd as rz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rz_fp8.h")
+
+RZ_OK, RZ_ERR_NULL, RZ_ERR_QTYPE, RZ_ERR_SHAPE, RZ_ERR_ALIGN, RZ_ERR_HIP, RZ_ERR_VALUE = 0, -1, -2, -3, -4, -5, -6
+P = 0x7F0000001000      # fake, 16-byte aligned, never dereferenced
+P2 = 0x7F0000002000
+P3 = 0x7F0000003000
+BAD = 0x7F0000001004     # 4-byte but not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rz_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rz.lib_path()):
+        pytest.skip("librz_fp8.so not built")
+    return rz.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert len(decl) >= 15
+    for name in decl:
+        assert hasattr(L, name), name
+    assert set(decl) == set(rz.EXPORTED)
+
+
+def test_sizes(L):
+    assert L.rz_block_bytes(12) == 144 and L.rz_block_bytes(14) == 210 and L.rz_block_bytes(2) == 0
+    assert L.rz_weight_bytes(12, 18944, 3584) == 18944 * 14 * 144
+    assert L.rz_weight_bytes(14, 3584, 18944) == 3584 * 74 * 210
+    assert L.rz_weight_bytes(12, 4, 300) == 0
+    assert [L.rz_pad_m(m) for m in (0, 1, 4, 16, 17, 37, 1000, 2048)] == [0, 16, 16, 16, 32, 48, 1008, 2048]
+    assert L.rz_workspace_bytes() >= 8192 + 16
+    assert L.rz_version().decode().startswith("rz_fp8")
+    assert L.rz_status_string(-3).decode() == "invalid shape"
+
+
+def _err(L):
+    return L.rz_last_error_string().decode()
+
+
+def test_pack_validation(L):
+    f = L.rz_fp8_pack_weight
+    host = ctypes.c_float()
+    h = ctypes.addressof(host)
+    assert f(12, None, 4, 256, P2, h, None, P3, None) == RZ_ERR_NULL
+    assert f(12, P, 4, 256, None, h, None, P3, None) == RZ_ERR_NULL
+    assert f(12, P, 4, 256, P2, None, None, P3, None) == RZ_ERR_NULL
+    assert f(12, P, 4, 256, P2, h, None, None, None) == RZ_ERR_NULL
+    assert f(2, P, 4, 256, P2, h, None, P3, None) == RZ_ERR_QTYPE
+    assert "unsupported qtype" in _err(L)
+    assert f(12, P, 4, 300, P2, h, None, P3, None) == RZ_ERR_SHAPE
+    assert f(14, P, 4, 0, P2, h, None, P3, None) == RZ_ERR_SHAPE
+    assert f(12, P, 0, 256, P2, h, None, P3, None) == RZ_ERR_SHAPE
+    assert f(12, P, 1 << 30, 1 << 20, P2, h, None, P3, None) == RZ_ERR_SHAPE
+    assert f(12, BAD, 4, 256, P2, h, None, P3, None) == RZ_ERR_ALIGN
+    assert f(12, P, 4, 256, BAD, h, None, P3, None) == RZ_ERR_ALIGN
+    assert host.value == 0.0  # outputs untouched on error
+
+
+def test_quant_act_validation(L):
+    f = L.rz_fp8_quant_act
+    assert f(None, 4, 256, P2, P3, P, None) == RZ_ERR_NULL
+    assert f(P, 4, 256, None, P3, P, None) == RZ_ERR_NULL
+    assert f(P, 4, 256, P2, None, P, None) == RZ_ERR_NULL
+    assert f(P, 4, 256, P2, P3, None, None) == RZ_ERR_NULL
+    assert f(P, 4, 100, P2, P3, P, None) == RZ_ERR_SHAPE
+    assert f(P, 4, 0, P2, P3, P, None) == RZ_ERR_SHAPE
+    assert f(BAD, 4, 256, P2, P3, P, None) == RZ_ERR_ALIGN
+    assert f(P, 4, 256, BAD, P3, P, None) == RZ_ERR_ALIGN
+    assert f(P, 4, 256, P2, P3 + 2, P, None) == RZ_ERR_ALIGN
+    assert f(None, 0, 256, None, None, P, None) == RZ_ERR_NULL  # the scale output is always written
+
+
+def test_gemm_validation(L):
+    f = L.rz_fp8_gemm
+    assert f(None, P2, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_NULL
+    assert f(P, None, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 256, None, 1.0, P, None) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 256, P3, 1.0, None, None) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 255, P3, 1.0, P, None) == RZ_ERR_SHAPE
+    assert f(P, P2, 4, 8, 0, P3, 1.0, P, None) == RZ_ERR_SHAPE
+    assert f(P, P2, 1 << 20, 1 << 20, 256, P3, 1.0, P, None) == RZ_ERR_SHAPE
+    assert f(BAD, P2, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_ALIGN
+    assert f(P, P2, 4, 8, 256, P3, 1.0, BAD, None) == RZ_ERR_ALIGN
+    assert f(P, P2, 4, 8, 256, P3, float("nan"), P, None) == RZ_ERR_VALUE
+    assert f(P, P2, 4, 8, 256, P3, float("inf"), P, None) == RZ_ERR_VALUE
+    # empty products are no-ops that touch nothing (no device needed)
+    assert f(P, P2, 0, 8, 256, P3, 1.0, P, None) == RZ_OK
+    assert f(P, P2, 4, 0, 256, P3, 1.0, P, None) == RZ_OK
+    assert f(None, None, 0, 8, 256, None, 1.0, None, None) == RZ_OK
+    assert f(None, None, 0, 8, 255, None, 1.0, None, None) == RZ_ERR_SHAPE
+
+
+def test_diagnostics_validation(L):
+    assert L.rz_dequant_f32(12, None, 4, 256, P, None) == RZ_ERR_NULL
+    assert L.rz_dequant_f32(3, P, 4, 256, P2, None) == RZ_ERR_QTYPE
+    assert L.rz_dequant_f32(14, P, 4, 512 + 16, P2, None) == RZ_ERR_SHAPE
+    assert L.rz_dequant_f32(14, BAD, 4, 512, P2, None) == RZ_ERR_ALIGN
+    assert L.rz_absmax_f32(None, 4, P2, P3, None) == RZ_ERR_NULL
+    assert L.rz_absmax_f32(BAD, 4, P2, P3, None) == RZ_ERR_ALIGN
+    assert L.rz_absmax_f32(P, (1 << 36) + 1, P2, P3, None) == RZ_ERR_SHAPE
+    assert L.rz_e4m3_encode(P, 4, 1.0, None, None) == RZ_ERR_NULL
+    assert L.rz_e4m3_encode(None, 0, 1.0, None, None) == RZ_OK
+    assert L.rz_e4m3_encode(P, 4, 1.0, BAD, None) == RZ_ERR_ALIGN
+    assert L.rz_fp8_scales(None, 4, P2, P3, None) == RZ_ERR_NULL
+    assert L.rz_fp8_scales(P, 0, P2, P3, None) == RZ_OK
+    out = (ctypes.c_int32 * 4)()
+    assert L.rz_fp8_gemm_plan(2048, 18944, 3584, ctypes.cast(out, ctypes.c_void_p)) == RZ_OK
+    assert out[0] * out[1] > 0 and out[2] % 64 == 0 and out[3] > 0
+    assert L.rz_fp8_gemm_plan(16, 256, 300, ctypes.cast(out, ctypes.c_void_p)) == RZ_ERR_SHAPE
+
+
+def test_plans_cover_shapes(L):
+    # every workload shape gets a plan whose tiles cover the output
+    for m, n, k in [(16, 256, 512), (512, 3584, 3584), (512, 512, 3584), (2048, 18944, 3584),
+                    (2048, 3584, 18944), (4096, 18944, 3584), (1, 4608, 3584), (1000, 4608, 3584)]:
+        bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+        mp = rz.rz_pad_m(m)
+        assert wgs == -(-mp // bm) * -(-n // bn)
+        assert threads in (64, 128, 256, 512)
+
+
+def test_binding_refuses_host_tensors(L):
+    import torch
+    with pytest.raises(ValueError):
+        rz.rz_fp8_quant_act(torch.zeros(4, 256))

@@ -1,0 +1,288 @@
+"""GPU parity of each kernel against the CPU oracle (needs an MI355X).
+
+Bit-exact: E4M3 codes, dequantised fp32 weights, absmax and scales.
+GEMM: |y - y_ref| <= 2e-3 * dq_act * dq_w * sum_k |dec(a_k) dec(w_k)| per
+element, y_ref the oracle's exact sum times the two scales.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import e4m3, fp8_path, kquant
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rz():
+    import fp8_prefill_gemm_amd as rz
+    rz.lib()  # loud failure if the HIP library is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return rz
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f32_from_bits(bits):
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+# ------------------------------------------------------------------ encoder
+
+def test_encode_golden_and_classes(rz):
+    from tests.test_oracle_e4m3 import _class_representatives, _pins
+    pins = _pins()
+    xb = np.array([p[0] for p in pins] + list(_class_representatives()), dtype=np.uint32)
+    x = f32_from_bits(xb)
+    got = host(rz.rz_e4m3_encode(dev(x), 1.0))
+    np.testing.assert_array_equal(got, e4m3.encode_scaled(x, 1.0))
+    # the golden codes themselves (scale 1 makes every NaN positive)
+    for (bits, code), g in zip(pins, got[:len(pins)]):
+        if ((bits >> 23) & 0xFF) == 0xFF and (bits & 0x7FFFFF):
+            assert g == 0x7E
+        else:
+            assert g == code, hex(bits)
+
+
+@pytest.mark.parametrize("count", [0, 1, 15, 16, 17, 1000, 65536 + 7])
+@pytest.mark.parametrize("scale", [1.0, 448.0 / 3.75, 1e-3, 3.0e4, 0.0])
+def test_encode_random_scaled(rz, count, scale):
+    g = np.random.Generator(np.random.PCG64(count + 17))
+    x = (g.standard_normal(count) * np.exp2(g.integers(-20, 20, count))).astype(np.float32)
+    if count > 8:
+        x[:4] = [np.inf, -np.inf, np.nan, -0.0]
+    got = host(rz.rz_e4m3_encode(dev(x), scale))
+    np.testing.assert_array_equal(got, e4m3.encode_scaled(x, scale))
+
+
+def test_scales_bit_exact(rz):
+    g = np.random.Generator(np.random.PCG64(99))
+    a = np.exp2(g.uniform(-149, 127, 200_000)).astype(np.float32)
+    a[:6] = [0.0, 448.0, 1.0, np.inf, 1e-45, 3.4e38]
+    q, dq = rz.rz_fp8_scales(dev(a))
+    q, dq = host(q), host(dq)
+    ref = [fp8_path.scales_from_absmax(v) for v in a]
+    np.testing.assert_array_equal(q, np.array([r[0] for r in ref], np.float32))
+    np.testing.assert_array_equal(dq, np.array([r[1] for r in ref], np.float32))
+
+
+# ------------------------------------------------------------------ absmax
+
+@pytest.mark.parametrize("count", [0, 1, 3, 17, 1000, 1 << 20, (1 << 22) + 3])
+def test_absmax(rz, count):
+    g = np.random.Generator(np.random.PCG64(count))
+    x = g.standard_normal(count).astype(np.float32)
+    if count >= 17:
+        x[5] = np.nan
+        x[count // 2] = -37.5  # the maximum, negative, mid-tensor
+        x[3] = -0.0
+    out = host(rz.rz_absmax_f32(dev(x)))
+    assert out[0].view(np.uint32) == np.uint32(fp8_path.absmax_bits(x))
+
+
+def test_absmax_specials(rz):
+    for x in ([np.nan, np.nan], [-0.0], [1.0, -np.inf, np.nan], [1e-40, -3e-41]):
+        x = np.array(x, np.float32)
+        out = host(rz.rz_absmax_f32(dev(x)))
+        assert out[0].view(np.uint32) == np.uint32(fp8_path.absmax_bits(x))
+
+
+# ------------------------------------------------------------------ dequant
+
+SHAPES = [(1, 256), (3, 768), (256, 512), (37, 1280), (130, 3584)]
+
+
+@pytest.mark.parametrize("qtype", [W.Q4_K, W.Q6_K])
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_dequant_bit_exact(rz, qtype, n, k):
+    blocks = W.weight_blocks(qtype, 500 + n, n, k)
+    got = host(rz.rz_dequant_f32(qtype, dev(blocks), n, k))
+    want = kquant.dequant(qtype, blocks, n, k)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_dequant_golden_layout_blocks(rz):
+    # the hand-pinned one-hot blocks go through the GPU unchanged
+    from tests.test_oracle_kquant import UNIT_SCALES, _q4k_block, _q6k_block
+    q4 = []
+    for t in (0, 31, 32, 100, 127):
+        qs = bytearray(128)
+        qs[t] = 0x21
+        q4.append(_q4k_block(scales=UNIT_SCALES, qs=qs))
+    q4 = np.concatenate(q4)
+    got = host(rz.rz_dequant_f32(W.Q4_K, dev(q4), q4.shape[0], 256))
+    np.testing.assert_array_equal(got, kquant.dequant_q4k_blocks(q4))
+    q6 = []
+    for t in (0, 40, 100):
+        ql = bytearray(128)
+        ql[t] = 0x21
+        q6.append(_q6k_block(ql=ql))
+    q6.append(_q6k_block(scales=[-128] * 16, ql=bytes([0xFF] * 128), qh=bytes([0xFF] * 64)))
+    q6 = np.concatenate(q6)
+    got = host(rz.rz_dequant_f32(W.Q6_K, dev(q6), q6.shape[0], 256))
+    np.testing.assert_array_equal(got, kquant.dequant_q6k_blocks(q6))
+
+
+# ------------------------------------------------------------------ pack
+
+@pytest.mark.parametrize("qtype", [W.Q4_K, W.Q6_K])
+@pytest.mark.parametrize("n,k", SHAPES + [(512, 3584)])
+def test_pack_bit_exact(rz, qtype, n, k):
+    blocks = W.weight_blocks(qtype, 900 + n, n, k)
+    w8, scale, amax = rz.rz_fp8_pack_weight(qtype, dev(blocks), n, k)
+    r8, rdq, ra = fp8_path.pack_weight(qtype, blocks, n, k)
+    assert np.float32(amax).view(np.uint32) == ra.view(np.uint32)
+    assert np.float32(scale).view(np.uint32) == rdq.view(np.uint32)
+    np.testing.assert_array_equal(host(w8), r8)
+
+
+def test_pack_zero_weight(rz):
+    blocks = np.zeros((4 * 2, 144), np.uint8)
+    w8, scale, amax = rz.rz_fp8_pack_weight(W.Q4_K, dev(blocks), 4, 512)
+    assert amax == 0.0 and np.float32(scale) == np.float32(1 / 448)
+    assert (host(w8) == 0).all()
+
+
+def test_pack_reuses_workspace(rz):
+    ws = rz.workspace("cuda")
+    for seed, (n, k) in enumerate([(64, 512), (8, 256), (300, 1024)]):
+        blocks = W.q6k_blocks(seed, n, k)
+        w8, scale, amax = rz.rz_fp8_pack_weight(W.Q6_K, dev(blocks), n, k, ws=ws)
+        r8, rdq, ra = fp8_path.pack_weight(W.Q6_K, blocks, n, k)
+        assert np.float32(scale) == rdq and np.float32(amax) == ra
+        np.testing.assert_array_equal(host(w8), r8)
+
+
+# ------------------------------------------------------------------ activation
+
+@pytest.mark.parametrize("m,k,kind", [(16, 512, "normal"), (1, 3584, "student_t"),
+                                      (4, 3584, "student_t"), (37, 3584, "student_t"),
+                                      (1000, 3584, "student_t"), (512, 3584, "normal"),
+                                      (33, 256, "silu"), (5, 3584, "zero")])
+def test_quant_act_bit_exact(rz, m, k, kind):
+    x = W.Group(m, k, kind, 700 + m).activation()
+    a8, sc = rz.rz_fp8_quant_act(dev(x))
+    r8, ra, rdq = fp8_path.quant_act(x)
+    sc = host(sc)
+    assert sc[0].view(np.uint32) == ra.view(np.uint32)
+    assert sc[1].view(np.uint32) == rdq.view(np.uint32)
+    np.testing.assert_array_equal(host(a8), r8)
+
+
+def test_quant_act_empty(rz):
+    a8, sc = rz.rz_fp8_quant_act(torch.zeros((0, 512), device="cuda"))
+    assert a8.shape == (0, 512)
+    sc = host(sc)
+    assert sc[0] == 0.0 and sc[1] == np.float32(1 / 448)
+    # and through the C ABI with real buffers: nothing but the scales is written
+    x = torch.ones((1, 512), device="cuda")
+    a8 = torch.full((16, 512), 7, dtype=torch.uint8, device="cuda")
+    sc = torch.full((4,), -1.0, device="cuda")
+    ws = rz.workspace("cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert rz.lib().rz_fp8_quant_act(x.data_ptr(), 0, 512, a8.data_ptr(), sc.data_ptr(),
+                                     ws.data_ptr(), st) == 0
+    assert (host(a8) == 7).all()
+    sc = host(sc)
+    assert sc[0] == 0.0 and sc[1] == np.float32(1 / 448)
+
+
+def test_quant_act_nonfinite(rz):
+    x = W.act_normal(5, 3, 256)
+    x[0, 0], x[1, 7], x[2, 9] = np.nan, np.inf, -3.0
+    a8, sc = rz.rz_fp8_quant_act(dev(x))
+    r8, ra, rdq = fp8_path.quant_act(x)
+    sc = host(sc)
+    assert sc[0] == np.inf and ra == np.inf and sc[1] == rdq
+    np.testing.assert_array_equal(host(a8), r8)
+
+
+def test_quant_act_overwrites_pad_rows(rz):
+    x = W.act_normal(6, 20, 512)
+    a8 = torch.full((32, 512), 0x5A, dtype=torch.uint8, device="cuda")
+    rz.rz_fp8_quant_act(dev(x), a_fp8=a8)
+    got = host(a8)
+    assert (got[20:] == 0).all()
+    np.testing.assert_array_equal(got, fp8_path.quant_act(x)[0])
+
+
+# ------------------------------------------------------------------ GEMM
+
+def check_gemm(y, a8, w8, m, dqa, dqw):
+    yr = fp8_path.gemm(a8, w8, m, dqa, dqw)
+    tol = fp8_path.bound(a8, w8, m, dqa, dqw)
+    err = np.abs(y.astype(np.float64) - yr)
+    bad = err > tol
+    assert not bad.any(), f"{bad.sum()} elements out of bound; worst {err[bad].max()} at {np.argwhere(bad)[0]}"
+    assert (y[tol == 0] == 0).all()
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (16, 256, 512),      # config 1
+    (1, 64, 256), (4, 96, 512), (37, 200, 768), (17, 258, 256),  # ragged n, n % 4 != 0
+    (300, 130, 1024), (600, 520, 512),   # medium plan, ragged tiles
+    (512, 1024, 512), (1000, 640, 256),
+])
+def test_gemm_random_codes(rz, m, n, k):
+    g = np.random.Generator(np.random.PCG64(m * 7 + n))
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    mp = fp8_path.pad_m(m)
+    a8 = g.choice(codes, size=(mp, k))
+    a8[m:] = 0
+    w8 = g.choice(codes, size=(n, k))
+    sc = np.array([1.0, 0.0123, 0, 0], np.float32)
+    wdq = np.float32(0.00731)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), float(wdq)))
+    assert y.shape == (m, n)
+    check_gemm(y, a8, w8, m, sc[1], wdq)
+
+
+def test_gemm_large_plan_full(rz):
+    # a shape that takes the 256x256 plan, checked in full
+    m, n, k = 1024, 2048, 512
+    bn, bm, _, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+    assert (bn, bm) == (256, 256)
+    g = np.random.Generator(np.random.PCG64(1))
+    a8 = g.integers(0, 0x7F, size=(m, k)).astype(np.uint8) | (g.integers(0, 2, size=(m, k)) << 7).astype(np.uint8)
+    w8 = g.integers(0, 0x7F, size=(n, k)).astype(np.uint8)
+    sc = np.array([1.0, 0.5, 0, 0], np.float32)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), 0.25))
+    check_gemm(y, a8, w8, m, sc[1], np.float32(0.25))
+
+
+def test_gemm_identity_weight(rz):
+    k, n, m = 512, 64, 37
+    w8 = np.zeros((n, k), np.uint8)
+    w8[np.arange(n), 3 * np.arange(n)] = 0x38
+    g = np.random.Generator(np.random.PCG64(3))
+    a8 = g.integers(0, 0x7F, size=(48, k)).astype(np.uint8)
+    sc = np.array([1.0, 1.0, 0, 0], np.float32)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), 1.0))
+    np.testing.assert_array_equal(y, e4m3.decode(a8[:m, 3 * np.arange(n)]).astype(np.float32))
+
+
+def test_gemm_extreme_accumulation(rz):
+    # K = 18944 products of 448 * -448: the largest sum the workloads allow
+    k = 18944
+    a8 = np.full((16, k), 0x7E, np.uint8)
+    w8 = np.full((32, k), 0xFE, np.uint8)
+    sc = np.array([1.0, 1.0, 0, 0], np.float32)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), 3, dev(sc), 1.0))
+    assert (y == np.float32(-448.0 * 448.0 * k)).all()
+
+
+def test_gemm_zero_activation_gives_zero(rz):
+    w8, scale, _ = rz.rz_fp8_pack_weight(W.Q4_K, dev(W.q4k_blocks(1, 64, 3584)), 64, 3584)
+    x = np.zeros((37, 3584), np.float32)
+    a8, sc = rz.rz_fp8_quant_act(dev(x))
+    y = host(rz.rz_fp8_gemm(a8, w8, 37, sc, scale))
+    assert (y == 0).all() and not np.signbit(y).any()

@@ -1,0 +1,99 @@
+"""End-to-end parity of the path on the workload configurations (GPU).
+
+Each group quantises its activation once and reuses it for every GEMM that
+reads it (Q/K/V; gate/up), as the path prescribes.  Packed bytes, scales and
+activation codes are compared bit for bit with the oracle; GEMM outputs are
+compared element by element on every row for the small configurations and
+on sampled rows (the oracle computes those rows exactly) at full size.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import fp8_path
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rz():
+    import fp8_prefill_gemm_amd as rz
+    rz.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return rz
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_group(rz, grp, rows=None, check_bytes=True):
+    print(f"\n  group m={grp.m} k={grp.k} act={grp.act_kind} gemms={[g.name for g in grp.gemms]}", flush=True)
+    x = grp.activation()
+    ws = rz.workspace("cuda")
+    a8, sc = rz.rz_fp8_quant_act(dev(x), ws=ws)
+    r8, ra, rdq = fp8_path.quant_act(x)
+    torch.cuda.synchronize()
+    sch = sc.cpu().numpy()
+    assert sch[0] == ra and sch[1] == rdq
+    np.testing.assert_array_equal(a8.cpu().numpy(), r8)
+    for gm in grp.gemms:
+        blocks = W.weight_blocks(gm.qtype, gm.w_seed, gm.n, gm.k)
+        w8, wsc, wam = rz.rz_fp8_pack_weight(gm.qtype, dev(blocks), gm.n, gm.k, ws=ws)
+        rw8, rwdq, rwa = fp8_path.pack_weight(gm.qtype, blocks, gm.n, gm.k)
+        assert np.float32(wam) == rwa and np.float32(wsc) == rwdq, gm.name
+        if check_bytes:
+            np.testing.assert_array_equal(w8.cpu().numpy(), rw8)
+        y = rz.rz_fp8_gemm(a8, w8, grp.m, sc, wsc)
+        torch.cuda.synchronize()
+        sel = np.arange(grp.m) if rows is None else np.asarray(rows)
+        y_s = y[torch.from_numpy(sel).cuda()].cpu().numpy().astype(np.float64)
+        yr, tol = fp8_path.gemm_rows(r8, rw8, sel, rdq, rwdq)
+        err = np.abs(y_s - yr)
+        assert (err <= tol).all(), f"{gm.name}: {(err > tol).sum()} out of bound"
+        assert np.isfinite(y_s).all()
+        print(f"    {gm.name}: N={gm.n} K={gm.k} rows={len(sel)} max err/tol="
+              f"{np.max(err / np.where(tol > 0, tol, 1)):.3g}", flush=True)
+        del w8, y
+
+
+def test_config1(rz):
+    for grp in W.config_groups(1):
+        run_group(rz, grp)
+
+
+def test_config2_attention_qkv(rz):
+    for grp in W.config_groups(2):
+        run_group(rz, grp)
+
+
+@pytest.mark.parametrize("m", W.CFG5_M)
+def test_config5_small_m(rz, m):
+    for grp in W.config_groups(5, m=m):
+        run_group(rz, grp)
+
+
+def test_config5_zero_activation(rz):
+    for m in W.CFG5_M:
+        grp = W.config_groups(5, m=m)[0]
+        grp.act_kind = "zero"
+        run_group(rz, grp)
+
+
+def _sample_rows(m, count=64, seed=0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = set(g.choice(m, size=count - 4, replace=False).tolist()) | {0, 1, m - 2, m - 1}
+    return sorted(rows)
+
+
+def test_config3_ffn_full_size(rz):
+    for grp in W.config_groups(3):
+        run_group(rz, grp, rows=_sample_rows(grp.m, seed=grp.act_seed))
+
+
+@pytest.mark.parametrize("layer", [0, W.CFG4_LAYERS - 1])
+def test_config4_layer(rz, layer):
+    for grp in W.config_groups(4, layer=layer):
+        run_group(rz, grp, rows=_sample_rows(grp.m, seed=grp.act_seed))
