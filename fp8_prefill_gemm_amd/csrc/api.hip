@@ -152,6 +152,7 @@ int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t
                 const float* act_scale_dev, float w_scale, float* y, void* stream) {
     static const char* fn = "rz_fp8_gemm";
     if (int r = check_k(fn, k)) return r;
+    if (k > RZ_MAX_GEMM_K) return fail(RZ_ERR_SHAPE, "%s: k=%u exceeds %u", fn, k, (unsigned)RZ_MAX_GEMM_K);
     if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
     if (!a_fp8 || !w_fp8 || !act_scale_dev || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
     if ((uint64_t)n * k > RZ_MAX_ELEMS || (uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS ||

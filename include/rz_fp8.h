@@ -56,6 +56,10 @@ typedef enum {
 /* Largest accepted n*k (weights) and m*k (activations): 2^36 elements. */
 #define RZ_MAX_ELEMS ((uint64_t)1 << 36)
 
+/* Largest K rz_fp8_gemm accepts (its tile loads use 32-bit byte offsets
+ * over 256 rows of K bytes). */
+#define RZ_MAX_GEMM_K ((uint32_t)(1u << 24) - 256u)
+
 /* Bytes per super-block of 256 weights: 144 (Q4_K, 0.5625 B/weight, as the
  * gemm.rs page states) or 210 (Q6_K); 0 for any other type. */
 size_t rz_block_bytes(int qtype);
@@ -121,7 +125,8 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
  *   w_scale       the host scale from rz_fp8_pack_weight
  *   y             device out, fp32 [m][n] row-major (only rows < m written)
  * Products are accumulated in fp32 on the matrix cores (no fp16 stage).
- * m == 0 or n == 0 is a no-op (any pointer may then be NULL).
+ * k <= RZ_MAX_GEMM_K.  m == 0 or n == 0 is a no-op (any pointer may then
+ * be NULL).
  */
 int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                 uint32_t k, const float* act_scale_dev, float w_scale, float* y,

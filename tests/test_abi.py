@@ -99,6 +99,7 @@ def test_gemm_validation(L):
     assert f(P, P2, 4, 8, 256, P3, 1.0, None, None) == RZ_ERR_NULL
     assert f(P, P2, 4, 8, 255, P3, 1.0, P, None) == RZ_ERR_SHAPE
     assert f(P, P2, 4, 8, 0, P3, 1.0, P, None) == RZ_ERR_SHAPE
+    assert f(P, P2, 4, 8, 1 << 24, P3, 1.0, P, None) == RZ_ERR_SHAPE
     assert f(P, P2, 1 << 20, 1 << 20, 256, P3, 1.0, P, None) == RZ_ERR_SHAPE
     assert f(BAD, P2, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_ALIGN
     assert f(P, P2, 4, 8, 256, P3, 1.0, BAD, None) == RZ_ERR_ALIGN

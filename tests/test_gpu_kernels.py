@@ -248,7 +248,7 @@ def test_gemm_random_codes(rz, m, n, k):
 
 def test_gemm_large_plan_full(rz):
     # a shape that takes the 256x256 plan, checked in full
-    m, n, k = 1024, 2048, 512
+    m, n, k = 2048, 8192, 256
     bn, bm, _, wgs = rz.rz_fp8_gemm_plan(m, n, k)
     assert (bn, bm) == (256, 256)
     g = np.random.Generator(np.random.PCG64(1))
