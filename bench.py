@@ -63,9 +63,10 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(x_ffn, gate_blocks, gate, m_rows=64):
-    """Time the oracle on a bounded sample: pack the gate weight, quantise the
-    FFN input, compute 64 output rows of the gate GEMM."""
+def cpu_baseline(x_ffn, x_down, gate_blocks, down_blocks, gate, dn, m_rows=128):
+    """Time the oracle on a bounded sample of the step: pack the gate and down
+    weights, quantise both inputs, compute m_rows output rows of the gate and
+    down GEMMs."""
     import numpy as np
     try:
         threads = len(os.sched_getaffinity(0))
@@ -78,29 +79,34 @@ def cpu_baseline(x_ffn, gate_blocks, gate, m_rows=64):
     except Exception:  # pragma: no cover - threadpoolctl missing
         limiter = None
     from oracle import fp8_path
-    t0 = time.perf_counter()
-    w8, dq_w, _ = fp8_path.pack_weight(gate.qtype, gate_blocks, gate.n, gate.k)
-    t1 = time.perf_counter()
+    t = [time.perf_counter()]
+    wg8, dq_g, _ = fp8_path.pack_weight(gate.qtype, gate_blocks, gate.n, gate.k)
+    t.append(time.perf_counter())
+    wd8, dq_d, _ = fp8_path.pack_weight(dn.qtype, down_blocks, dn.n, dn.k)
+    t.append(time.perf_counter())
     a8, _, dq_a = fp8_path.quant_act(x_ffn)
-    t2 = time.perf_counter()
+    d8, _, dq_x = fp8_path.quant_act(x_down)
+    t.append(time.perf_counter())
     rows = np.linspace(0, x_ffn.shape[0] - 1, m_rows).astype(np.int64)
-    fp8_path.gemm_rows(a8, w8, rows, dq_a, dq_w)
-    t3 = time.perf_counter()
+    fp8_path.gemm_rows(a8, wg8, rows, dq_a, dq_g)
+    fp8_path.gemm_rows(d8, wd8, rows, dq_x, dq_d)
+    t.append(time.perf_counter())
     if limiter is not None:
         limiter.restore_original_limits()
-    flops = 2.0 * m_rows * gate.n * gate.k
-    total = t3 - t0
-    log(f"cpu oracle: pack {t1 - t0:.2f}s quant {t2 - t1:.2f}s gemm({m_rows} rows) {t3 - t2:.2f}s")
+    flops = 2.0 * m_rows * (gate.n * gate.k + dn.n * dn.k)
+    total = t[-1] - t[0]
+    log(f"cpu oracle: pack gate {t[1] - t[0]:.2f}s pack down {t[2] - t[1]:.2f}s quant {t[3] - t[2]:.2f}s "
+        f"gemm({m_rows} rows x2) {t[4] - t[3]:.2f}s")
     return {
         "value": flops / total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle (numpy) on the gate GEMM of the same workload: pack the full "
-                   f"{gate.n}x{gate.k} Q4_K weight ({t1 - t0:.2f}s), quantise the full "
-                   f"{x_ffn.shape[0]}x{x_ffn.shape[1]} input ({t2 - t1:.2f}s), exact GEMM of "
-                   f"{m_rows} of {x_ffn.shape[0]} output rows ({t3 - t2:.2f}s); value = those "
-                   f"rows' 2*m*N*K FLOPs / total time; BLAS threads = cores"),
+        "sample": (f"oracle (numpy) on a slice of the same step: pack the full {gate.n}x{gate.k} Q4_K gate "
+                   f"weight ({t[1] - t[0]:.2f}s) and {dn.n}x{dn.k} Q6_K down weight ({t[2] - t[1]:.2f}s), "
+                   f"quantise both full inputs ({t[3] - t[2]:.2f}s), exact gate and down GEMMs for {m_rows} of "
+                   f"{x_ffn.shape[0]} output rows ({t[4] - t[3]:.2f}s); value = those rows' 2*m*N*K FLOPs / "
+                   f"total time ({total:.1f}s); cores = BLAS threads"),
     }
 
 
@@ -240,7 +246,7 @@ def main() -> int:
             "m": M, "gate_up": [gate.n, gate.k], "down": [dn.n, dn.k],
         },
         "roofline": {
-            "kernel": f"fp8_gemm_kernel<{plan[0]},{plan[1]}> (gate/up, M=2048 N=18944 K=3584)",
+            "kernel": f"gate/up GEMM, {plan[0]}x{plan[1]} tiles (M=2048 N=18944 K=3584)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP8_PEAK_TFLOPS,
@@ -254,7 +260,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(x_ffn_h, gate_blocks_h, gate)
+        out["cpu_baseline"] = cpu_baseline(x_ffn_h, x_down_h, gate_blocks_h, down_blocks_h, gate, dn)
     print(json.dumps(out), flush=True)
     return 0
 
