@@ -164,6 +164,8 @@ def main() -> int:
     sc_down = torch.empty(4, dtype=f32, device=dev)
     y = {g.name: torch.empty((M, g.n), dtype=f32, device=dev) for g in (gate, up, dn)}
     ws = rz.workspace(dev)
+    gws_bytes = max(rz.rz_fp8_gemm_workspace_bytes(M, g.n, g.k) for g in (gate, up, dn))
+    gws = torch.zeros(max(gws_bytes, 256), dtype=u8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration:
@@ -191,13 +193,13 @@ def main() -> int:
         mark(3)
         rz.rz_fp8_quant_act(x_ffn, a8_ffn, sc_ffn, ws, stream)
         mark(4)
-        rz.rz_fp8_gemm(a8_ffn, w8["gate"], M, sc_ffn, scales["gate"], y["gate"], stream)
+        rz.rz_fp8_gemm(a8_ffn, w8["gate"], M, sc_ffn, scales["gate"], y["gate"], stream, gws)
         mark(5)
-        rz.rz_fp8_gemm(a8_ffn, w8["up"], M, sc_ffn, scales["up"], y["up"], stream)
+        rz.rz_fp8_gemm(a8_ffn, w8["up"], M, sc_ffn, scales["up"], y["up"], stream, gws)
         mark(6)
         rz.rz_fp8_quant_act(x_down, a8_down, sc_down, ws, stream)
         mark(7)
-        rz.rz_fp8_gemm(a8_down, w8["down"], M, sc_down, scales["down"], y["down"], stream)
+        rz.rz_fp8_gemm(a8_down, w8["down"], M, sc_down, scales["down"], y["down"], stream, gws)
         mark(8)
 
     log(f"warmup {args.warmup} steps")

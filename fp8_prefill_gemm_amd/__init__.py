@@ -41,7 +41,8 @@ _SIGS = {
     "rz_workspace_bytes": (ctypes.c_size_t, []),
     "rz_fp8_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "rz_fp8_quant_act": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp, _vp]),
-    "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp]),
+    "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
+    "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
     "rz_dequant_f32": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
     "rz_absmax_f32": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_e4m3_encode": (_i32, [_vp, _u64, _f32, _vp, _vp]),
@@ -164,16 +165,44 @@ def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
     return a_fp8, act_scale
 
 
-def rz_fp8_gemm(a_fp8, w_fp8, m: int, act_scale, w_scale: float, y=None, stream=None):
-    """-> y fp32 [m][n] = dec(a)[:m] @ dec(w)^T * act_scale[1] * w_scale."""
+_gemm_ws = {}
+
+
+def gemm_workspace(device, nbytes: int):
+    """A zero-filled GEMM workspace of at least `nbytes`, cached per device.
+
+    The GEMM returns its workspace to the zero state, so one buffer serves
+    every call issued in order on one stream."""
+    torch = _torch()
+    key = torch.device(device).index or 0
+    buf = _gemm_ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _gemm_ws[key] = buf
+    return buf
+
+
+def rz_fp8_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().rz_fp8_gemm_workspace_bytes(m, n, k))
+
+
+def rz_fp8_gemm(a_fp8, w_fp8, m: int, act_scale, w_scale: float, y=None, stream=None, ws="auto"):
+    """-> y fp32 [m][n] = dec(a)[:m] @ dec(w)^T * act_scale[1] * w_scale.
+
+    ws: "auto" (a cached zero-filled workspace sized for the shape), None (no
+    workspace: no K split), or a zero-filled uint8 device tensor."""
     torch = _torch()
     _require_cuda(a_fp8, w_fp8, act_scale, y)
     n, k = w_fp8.shape
     dev = w_fp8.device
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if isinstance(ws, str):
+        need = rz_fp8_gemm_workspace_bytes(m, n, k)
+        ws = gemm_workspace(dev, need) if need else None
+    _require_cuda(ws)
     _check(lib().rz_fp8_gemm(_ptr(a_fp8), _ptr(w_fp8), m, n, k, _ptr(act_scale), float(w_scale),
-                             _ptr(y), _stream(stream, dev)))
+                             _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, dev)))
     return y
 
 

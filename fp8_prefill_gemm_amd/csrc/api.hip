@@ -41,6 +41,7 @@ bool qtype_ok(int q) { return q == RZ_Q4_K || q == RZ_Q6_K; }
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 ok, -1 unsupported
+int g_dev_cus[kMaxDevices];    // compute units of each checked device
 
 int check_device(const char* fn) {
     int dev = 0;
@@ -53,12 +54,29 @@ int check_device(const char* fn) {
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return hip_fail(e, fn);
         g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_cus[dev] = prop.multiProcessorCount;
         if (g_dev_state[dev] < 0)
             return fail(RZ_ERR_HIP, "%s: device %d is %s; this library is built for gfx950 only", fn,
                         dev, prop.gcnArchName);
     }
     if (g_dev_state[dev] < 0) return fail(RZ_ERR_HIP, "%s: device %d is not gfx950", fn, dev);
     return RZ_OK;
+}
+
+// Compute units of the current device for GEMM planning (MI355X: 256).  Used
+// only to size persistent grids; falls back to 256 when no device answers.
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (g_dev_cus[dev] > 0) return g_dev_cus[dev];
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+            g_dev_cus[dev] = cus;
+            return cus;
+        }
+    }
+    return 256;
 }
 
 int check_k(const char* fn, uint32_t k) {
@@ -149,7 +167,8 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, flo
 }
 
 int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n, uint32_t k,
-                const float* act_scale_dev, float w_scale, float* y, void* stream) {
+                const float* act_scale_dev, float w_scale, float* y, void* ws, size_t ws_bytes,
+                void* stream) {
     static const char* fn = "rz_fp8_gemm";
     if (int r = check_k(fn, k)) return r;
     if (k > RZ_MAX_GEMM_K) return fail(RZ_ERR_SHAPE, "%s: k=%u exceeds %u", fn, k, (unsigned)RZ_MAX_GEMM_K);
@@ -158,24 +177,31 @@ int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t
     if ((uint64_t)n * k > RZ_MAX_ELEMS || (uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS ||
         (uint64_t)m * n > RZ_MAX_ELEMS || m > 0x7FFFFFF0u || n > 0x7FFFFFF0u)
         return fail(RZ_ERR_SHAPE, "%s: operand too large", fn);
-    if (!aligned16(a_fp8) || !aligned16(w_fp8) || !aligned16(y) || ((uintptr_t)act_scale_dev & 3u))
+    if (!aligned16(a_fp8) || !aligned16(w_fp8) || !aligned16(y) || ((uintptr_t)act_scale_dev & 3u) ||
+        (ws && !aligned16(ws)))
         return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     if (w_scale != w_scale || w_scale - w_scale != 0.0f)
         return fail(RZ_ERR_VALUE, "%s: w_scale must be finite", fn);
     if (int r = check_device(fn)) return r;
-    hipError_t e = rz::launch_gemm(a_fp8, w_fp8, m, n, k, act_scale_dev, w_scale, y, as_stream(stream));
+    hipError_t e = rz::launch_gemm(a_fp8, w_fp8, m, n, k, act_scale_dev, w_scale, y, ws, ws ? ws_bytes : 0,
+                                   device_cus(), as_stream(stream));
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k) {
+    if (k == 0 || k % 256u != 0 || m == 0 || n == 0) return 0;
+    return rz::plan_gemm(m, n, k, device_cus(), true).ws_bytes;
 }
 
 int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out) {
     static const char* fn = "rz_fp8_gemm_plan";
     if (!cfg_out) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
     if (int r = check_k(fn, k)) return r;
-    const rz::GemmPlan p = rz::plan_gemm(m, n, k);
+    const rz::GemmPlan p = rz::plan_gemm(m, n, k, device_cus(), true);
     cfg_out[0] = p.bn;
     cfg_out[1] = p.bm;
     cfg_out[2] = p.threads;
-    cfg_out[3] = (m == 0 || n == 0) ? 0 : p.workgroups;
+    cfg_out[3] = (m == 0 || n == 0) ? 0 : p.workgroups + (p.s > 1 ? p.split_workgroups : 0);
     return RZ_OK;
 }
 

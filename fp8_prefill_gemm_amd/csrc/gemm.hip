@@ -144,20 +144,7 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* st
     }
 }
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
-
-// One 128-byte K-step of the pipelined kernel for one wave (256x256 tile,
-// 2x2 waves of 128x128, so TN = TM = 4).  The step is one basic block:
-//   * all 8 weight fragments of the step (both 64-byte halves) and the first
-//     activation fragment are read up front; every later activation fragment
-//     is read one MFMA group ahead into the other half of a double buffer;
-//   * the 16 stage stores of the next K-step (staged one step earlier, into
-//     the other LDS slot) and the 16 buffer loads of the K-step after that
-//     are spread between the 32 MFMAs;
-// so the matrix pipe always has queued work while LDS and memory traffic
-// proceed.  The caller puts a barrier after each step.
-// Per-lane LDS offsets of the pipelined kernel, computed once.  The swizzle
+// Per-lane LDS offsets of the persistent kernel, computed once.  The swizzle
 // only depends on row bits 0..4, so every row the lane touches (its own row
 // plus multiples of 32) shares it and all addresses differ by immediates.
 struct PipeOffsets {
@@ -188,155 +175,298 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* base, uint32_t lo, uint32_
     return __builtin_bit_cast(v8i, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One 128-byte K-step of the pipelined kernel for one wave (256x256 tile,
-// 2x2 waves of 128x128, so TN = TM = 4).  The step is one basic block:
-//   * all 8 weight fragments of the step (both 64-byte halves) and the first
-//     activation fragment are read up front; every later activation fragment
-//     is read one MFMA group ahead into the other half of a double buffer;
-//   * the 16 stage stores of the next K-step (staged one step earlier, into
-//     the other LDS slot) and the 16 buffer loads of the K-step after that
-//     are spread between the 32 MFMAs;
-// so the matrix pipe always has queued work while LDS and memory traffic
-// proceed.  The caller puts a barrier after each step.
-template <int LG>
-__device__ __forceinline__ void pipe_step(v16f (&acc)[4][4], const uint8_t* cur, uint8_t* nxt,
-                                          const u32x4 (&st)[LG], u32x4 (&ld)[LG],
-                                          __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars,
-                                          uint32_t voff, uint32_t kb_next, uint32_t step,
-                                          const PipeOffsets& o) {
+// One 128-byte K-step of the persistent kernel for one wave (256x256 tile,
+// 2x2 waves of 128x128: 4x4 MFMA tiles of 32x32, two 64-byte K halves).
+//   cur  LDS slot holding this step's operands (weight rows, then activation
+//        rows, 128 bytes each);
+//   nxt  the other slot, which receives the next step's operands;
+//   x    16 staged 16-byte chunks per thread holding the next step's data
+//        (chunks 0..7 weight rows tid/8 + 32c, 8..15 activation rows); each
+//        is written to `nxt` and then refilled from global memory with the
+//        K-step three ahead of this one (byte offset kb; rsrc wrs / ars).
+// The step is eight MFMA groups (one activation fragment against the four
+// weight fragments of one K half).  A sched_barrier closes every group, so
+// the program order is exactly: fragment reads for the next group, 4 MFMAs,
+// 2 chunk writes, 2 chunk loads.  A chunk load therefore has two full steps
+// to land before the same group of the step after next writes it to LDS.
+// The caller places a workgroup barrier after each step.
+__device__ __forceinline__ void kstep(v16f (&acc)[4][4], const uint8_t* cur, uint8_t* nxt, u32x4 (&x)[16],
+                                      __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars, uint32_t voff,
+                                      uint32_t kb, uint32_t step, const PipeOffsets& o) {
     constexpr int kRow32 = 32 * kBK;  // 32 rows
     v8i a[2][4];
     v8i b[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[kk][i] = frag_at(cur + i * kRow32, o.fa[kk][0], o.fa[kk][1]);
+    for (int i = 0; i < 4; ++i) a[0][i] = frag_at(cur + i * kRow32, o.fa[0][0], o.fa[0][1]);
     b[0] = frag_at(cur, o.fb[0][0], o.fb[0][1]);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         const int kk = g >> 2, j = g & 3;
         if (g < 7) {
-            const int kn = (g + 1) >> 2, jn = (g + 1) & 3;
-            b[(g + 1) & 1] = frag_at(cur + jn * kRow32, o.fb[kn][0], o.fb[kn][1]);
+            const int gn = g + 1;
+            b[gn & 1] = frag_at(cur + (gn & 3) * kRow32, o.fb[gn >> 2][0], o.fb[gn >> 2][1]);
+        }
+        if (g == 1 || g == 2) {  // second K half's weight fragments, two per group
+#pragma unroll
+            for (int i = 2 * (g - 1); i < 2 * g; ++i) a[1][i] = frag_at(cur + i * kRow32, o.fa[1][0], o.fa[1][1]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[g & 1], acc[i][j], 0,
-                                                                        0, 0, 0, 0, 0);
-        // two stage stores and two prefetch loads per MFMA group; chunk c < 8
-        // is weight row block c, c >= 8 activation row block c-8
-#pragma unroll
-        for (int c = 2 * g; c < 2 * g + 2; ++c)
-            *reinterpret_cast<u32x4*>(nxt + (c / (LG / 2)) * 256 * kBK + (c % (LG / 2)) * kRow32 + o.st) = st[c];
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[g & 1], acc[i][j], 0, 0, 0,
+                                                                        0, 0, 0);
 #pragma unroll
         for (int c = 2 * g; c < 2 * g + 2; ++c) {
-            const __amdgpu_buffer_rsrc_t rs = c < LG / 2 ? wrs : ars;
-            ld[c] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, kb_next + (c % (LG / 2)) * step, 0));
+            *reinterpret_cast<u32x4*>(nxt + (c >> 3) * 256 * kBK + (c & 7) * kRow32 + o.st) = x[c];
+            x[c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, kb + (c & 7) * step, 0));
         }
-    }
-    // interleave: per group, 2 fragment reads, 4 MFMAs with the 2 stores
-    // and 2 loads between them (the 10 up-front reads go first)
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 10, 0);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        if (g < 7) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// 256x256 tile, 4 waves, fully software-pipelined K loop (interior tiles
-// only: every row of the tile exists in both operands).  Register sets:
-// set 0 / set 1 alternate between "being stored to LDS this step" and
-// "being loaded for two steps ahead".  Loads past the last K-step re-read
-// K-step 0 (their data is stored to the idle slot and never read).
-__global__ __launch_bounds__(256) void fp8_gemm_pipe_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
-    int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
-    int tiles_n, int group_m) {
-    constexpr int BN = 256, BM = 256, NT = 256, LG = 16;  // 8 weight + 8 activation chunks
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BN + BM) * kBK];
+// ---------------------------------------------------------------------------
+// Interior 256x256 tiles.
+//
+// When padded M and N are multiples of 256 the output splits into T whole
+// tiles.  G = one workgroup per CU; the first R*G tiles (R = floor(T/G) full
+// rounds, chosen as whole n-columns of tiles) run one tile per workgroup in
+// fp8_gemm_tile_kernel.  The rem = T - R*G tiles left over would leave most
+// CUs idle for a whole tile time, so fp8_gemm_split_kernel splits each of
+// them along K into s chunks (s*rem <= G) that run in parallel; the chunks
+// store partial sums in a workspace and count themselves in, and the last to
+// arrive adds the s partials in chunk order (so the result does not depend on
+// the arrival order) and writes the output.  No workgroup waits for another.
+//
+// Both kernels run the same K loop (tile_mainloop): two LDS slots, the global
+// loads three K-steps ahead of the MFMAs in two register sets.
+// ---------------------------------------------------------------------------
 
-    const int T = tiles_m * tiles_n;
+// Origin of tile t in the grouped order of a tiles_m x tiles_n region
+// (groups of gm m-tiles, m fastest inside a group).
+__device__ __forceinline__ void grouped_origin(int t, int tiles_m, int tiles_n, int gm_full, int& n0,
+                                               int& m0) {
+    const int per_group = gm_full * tiles_n;
+    const int gidx = t / per_group;
+    const int first_m = gidx * gm_full;
+    const int gm = (tiles_m - first_m) < gm_full ? (tiles_m - first_m) : gm_full;
+    const int tin = t - gidx * per_group;
+    n0 = (tin / gm) * 256;
+    m0 = (first_m + tin % gm) * 256;
+}
+
+// acc (or acc*scale) over the K-steps [k0, k0+KS) of the tile whose weight
+// rows start at `wrs` and activation rows at `ars` (KS even, >= 4).
+//
+// K-step t computes from LDS slot t%2 while register set (t%2 ? xq : xp)
+// moves the data of step t+1 into the other slot and is refilled with step
+// t+3; so each load has two steps of MFMA work to land.
+__device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][4], uint8_t (&smem)[2][512 * kBK],
+                                              __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars,
+                                              uint32_t voff, uint32_t step, int k0, int KS,
+                                              const PipeOffsets& po) {
+    const __amdgpu_buffer_rsrc_t zr = tile_rsrc(nullptr, 0u);  // range 0: loads return 0, no traffic
+    const uint32_t kb0 = (uint32_t)k0 * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+    u32x4 xp[16], xq[16];
+    // K-step 0 -> slot 0 (through xq), K-step 1 -> xp, K-step 2 -> xq
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        xq[c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, kb0 + (c & 7) * step, 0));
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        xp[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff,
+                                                                                kb0 + kBK + (c & 7) * step, 0));
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        *reinterpret_cast<u32x4*>(smem[0] + (c >> 3) * 256 * kBK + (c & 7) * 32 * kBK + po.st) = xq[c];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        xq[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              c < 8 ? wrs : ars, voff, kb0 + 2 * kBK + (c & 7) * step, 0));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < KS; kt += 2) {
+        const bool in3 = kt + 3 < KS, in4 = kt + 4 < KS;
+        kstep(acc, smem[0], smem[1], xp, in3 ? wrs : zr, in3 ? ars : zr, voff, kb0 + (uint32_t)(kt + 3) * kBK, step,
+              po);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(acc, smem[1], smem[0], xq, in4 ? wrs : zr, in4 ? ars : zr, voff, kb0 + (uint32_t)(kt + 4) * kBK, step,
+              po);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// acc * scale -> the tile's rows of Y (float4 runs of n).  `yrs` covers the
+// tile's valid rows only, so the stores of rows m >= M fall outside the
+// buffer range and are dropped by the hardware (no branches).
+__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t yrs, int N, int n0,
+                                           int wn, int wm, int lane, float scale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t row = (uint32_t)(wm * 128 + j * 32 + (lane & 31));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t n = (uint32_t)(n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
+                const float4 v = make_float4(acc[i][j][4 * q] * scale, acc[i][j][4 * q + 1] * scale,
+                                             acc[i][j][4 * q + 2] * scale, acc[i][j][4 * q + 3] * scale);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yrs,
+                                                       (row * (uint32_t)N + n) * 4u, 0, 0);
+            }
+        }
+    }
+}
+
+// Rows [m0, min(m0+256, M)) of Y; the planner keeps 256*N*4 below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M, int N, int m0) {
+    const int rows = (M - m0) < 256 ? (M - m0) : 256;
+    return __builtin_amdgcn_make_buffer_rsrc(Y + (size_t)m0 * N, (short)0, rows * N * 4, 0x00020000);
+}
+
+// One interior tile per workgroup over the first T tiles of the grouped
+// order (T = gridDim.x).  The dispatcher sends workgroup w to XCD w % 8, so
+// XCD x is given the contiguous range of tiles [x*T/8, (x+1)*T/8): the
+// workgroups that run together on one XCD share weight and activation rows
+// through its L2.
+__global__ __launch_bounds__(256) void fp8_gemm_tile_kernel(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ Wt, float* __restrict__ Y,
+                                                            int M, int N, int K, const float* __restrict__ act_scale,
+                                                            float w_scale, int tiles_m, int tiles_n, int group_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
+    const int T = (int)gridDim.x;
     const int w = blockIdx.x;
     const int tall = T / kXcds, rem = T % kXcds;
     const int x = w % kXcds, loc = w / kXcds;
     const int t = x * tall + (x < rem ? x : rem) + loc;
-    const int per_group = group_m * tiles_n;
-    const int gidx = t / per_group;
-    const int first_m = gidx * group_m;
-    const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int tin = t - gidx * per_group;
-    const int n0 = (tin / gm) * BN;
-    const int m0 = (first_m + tin % gm) * BM;
+    int n0, m0;
+    grouped_origin(t, tiles_m, tiles_n, group_m, n0, m0);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int wn = wid & 1, wm = wid >> 1;
+    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
+    const PipeOffsets po = pipe_offsets(tid, wn, wm, lane);
 
     v16f acc[4][4];
+    tile_mainloop(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, 0, K / kBK, po);
+    store_tile(acc, tile_out_rsrc(Y, M, N, m0), N, n0, wn, wm, lane, act_scale[1] * w_scale);
+}
+
+// Split tiles: the n-columns [nd, tiles_n) of tiles (all m), rem tiles in a
+// grouped order with groups of tail_gm m-tiles.  XCD x owns the tiles
+// [x*per_xcd, (x+1)*per_xcd) and its workgroups take them chunk by chunk, so
+// all s chunks of a tile run on one XCD, whose L2 is coherent for its CUs.
+// Chunk c covers the 256-byte K pairs [c*pairs/s, (c+1)*pairs/s).
+struct SplitPlan {
+    int tiles_m, nd, rem, tail_gm, per_xcd, s, pairs;
+};
+
+// Last arriver of a split tile: out = sum over chunks c = 0..S-1 (in that
+// order) of partial c, scaled.  Partials are thread-major float4 blocks:
+// block b = (i*4 + j)*4 + q of thread t at float offset (b*256 + t)*4.
+// NB blocks are loaded per batch (NB*S loads in flight per thread).
+template <int S, int NB>
+__device__ __forceinline__ void fixup_tile(const float* __restrict__ parts, __amdgpu_buffer_rsrc_t yrs, int N,
+                                           int n0, int wn, int wm, int lane, int tid, float scale) {
+    const __amdgpu_buffer_rsrc_t prs =
+        tile_rsrc(reinterpret_cast<const uint8_t*>(parts), (uint32_t)S * 256u * 256u * 4u);
+    for (int b0 = 0; b0 < 64; b0 += NB) {
+        u32x4 v[S][NB];
+#pragma unroll
+        for (int c = 0; c < S; ++c)
+#pragma unroll
+            for (int u = 0; u < NB; ++u)  // sc0: not from this CU's L1
+                v[c][u] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               prs, ((uint32_t)c * 65536u + (uint32_t)((b0 + u) * 256 + tid) * 4u) * 4u, 0, 1));
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int b = b0 + u;
+            const int i = b >> 4, j = (b >> 2) & 3, q = b & 3;
+            float4 sum = make_float4(__uint_as_float(v[0][u].x), __uint_as_float(v[0][u].y),
+                                     __uint_as_float(v[0][u].z), __uint_as_float(v[0][u].w));
+#pragma unroll
+            for (int c = 1; c < S; ++c) {
+                sum.x += __uint_as_float(v[c][u].x);
+                sum.y += __uint_as_float(v[c][u].y);
+                sum.z += __uint_as_float(v[c][u].z);
+                sum.w += __uint_as_float(v[c][u].w);
+            }
+            const uint32_t row = (uint32_t)(wm * 128 + j * 32 + (lane & 31));
+            const uint32_t n = (uint32_t)(n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
+            const float4 o = make_float4(sum.x * scale, sum.y * scale, sum.z * scale, sum.w * scale);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), yrs, (row * (uint32_t)N + n) * 4u, 0,
+                                                   0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void fp8_gemm_split_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M, int N, int K,
+    const float* __restrict__ act_scale, float w_scale, SplitPlan P, float* __restrict__ part,
+    unsigned* __restrict__ cnt) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
+    __shared__ unsigned arrival;
+
+    const int g = blockIdx.x;
+    const int x = g % kXcds, j = g / kXcds;
+    const int base = x * P.per_xcd;
+    int count = P.rem - base;
+    count = count < P.per_xcd ? count : P.per_xcd;
+    if (count <= 0 || j >= count * P.s) return;
+    const int tl = base + j / P.s, chunk = j % P.s;
+    int n0, m0;
+    grouped_origin(tl, P.tiles_m, (N >> 8) - P.nd, P.tail_gm, n0, m0);
+    n0 += P.nd * 256;
+    const int p0 = chunk * P.pairs / P.s, p1 = (chunk + 1) * P.pairs / P.s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int wn = wid & 1, wm = wid >> 1;
+    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
+    const PipeOffsets po = pipe_offsets(tid, wn, wm, lane);
+
+    v16f acc[4][4];
+    tile_mainloop(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, 2 * p0, 2 * (p1 - p0),
+                  po);
+
+    float* parts = part + (size_t)tl * P.s * (256 * 256);
+    float* mine = parts + (size_t)chunk * (256 * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
-
-    const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(Wt + (size_t)n0 * K, (uint32_t)BN * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t ars = tile_rsrc(A + (size_t)m0 * K, (uint32_t)BM * (uint32_t)K);
-    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
-    const uint32_t step = (uint32_t)(NT / 8) * (uint32_t)K;
-    const int KT = K / kBK;  // even
-
-    u32x4 s0[LG], s1[LG];
-    // prologue: K-step 0 -> slot 0 (through set 0), K-step 1 -> set 1
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-    for (int c = 0; c < LG; ++c)
-        s0[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              c < LG / 2 ? wrs : ars, voff, (c % (LG / 2)) * step, 0));
-#pragma unroll
-    for (int c = 0; c < LG; ++c)
-        s1[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              c < LG / 2 ? wrs : ars, voff, kBK + (c % (LG / 2)) * step, 0));
-    const PipeOffsets po = pipe_offsets(tid, wn, wm, lane);
-#pragma unroll
-    for (int c = 0; c < LG; ++c)
-        *reinterpret_cast<u32x4*>(smem[0] + (c / (LG / 2)) * BN * kBK + (c % (LG / 2)) * 32 * kBK + po.st) = s0[c];
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(mine + ((size_t)(((i * 4 + jj) * 4 + q) * 256 + tid) << 2)) =
+                    make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                                acc[i][jj][4 * q + 3]);
+    // All chunks of this tile run on this XCD, whose L2 is coherent for its
+    // CUs: wait until the stores have reached it, then count in.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-        // step kt: slot 0 computes, set 1 (K-step kt+1) -> slot 1, set 0 <- K-step kt+2
-        const uint32_t kb2 = (kt + 2 < KT) ? (uint32_t)(kt + 2) * kBK : 0u;
-        pipe_step<LG>(acc, smem[0], smem[1], s1, s0, wrs, ars, voff, kb2, step, po);
-        __syncthreads();
-        // step kt+1: slot 1 computes, set 0 (K-step kt+2) -> slot 0, set 1 <- K-step kt+3
-        const uint32_t kb3 = (kt + 3 < KT) ? (uint32_t)(kt + 3) * kBK : 0u;
-        pipe_step<LG>(acc, smem[1], smem[0], s0, s1, wrs, ars, voff, kb3, step, po);
-        __syncthreads();
-    }
-
-    const float s = act_scale[1] * w_scale;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + wm * 128 + j * 32 + (lane & 31);
-            if (m >= M) continue;
-            float* yrow = Y + (size_t)m * N;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
-                *reinterpret_cast<float4*>(yrow + n) =
-                    make_float4(acc[i][j][4 * g] * s, acc[i][j][4 * g + 1] * s, acc[i][j][4 * g + 2] * s,
-                                acc[i][j][4 * g + 3] * s);
-            }
-        }
+    if (tid == 0) arrival = __hip_atomic_fetch_add(cnt + tl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != (unsigned)(P.s - 1)) return;
+    if (tid == 0)  // ready the counter for the next call
+        __hip_atomic_store(cnt + tl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t yrs = tile_out_rsrc(Y, M, N, m0);
+    const float scale = act_scale[1] * w_scale;
+    switch (P.s) {
+        case 2: fixup_tile<2, 16>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
+        case 3: fixup_tile<3, 16>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
+        default: fixup_tile<4, 8>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
     }
 }
 
@@ -555,64 +685,119 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     }
 }
 
-enum Kind { kLarge = 0, kMedium = 1, kSmall = 2 };
+enum Kind { kTiles = 0, kMedium = 1, kSmall = 2, kLargeEdge = 3 };
 
 struct KindInfo {
     int bn, bm, threads;
 };
-constexpr KindInfo kKinds[3] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}};
+constexpr KindInfo kKinds[4] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}, {256, 256, 256}};
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Arrival counters of the split tiles (one uint32 each), padded to 256 bytes;
+// the partial sums follow.
+size_t split_counter_bytes(int rem) { return ((size_t)rem * sizeof(unsigned) + 255) / 256 * 256; }
+
 }  // namespace
 
-GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k) {
-    (void)k;
+// Kernel choice per shape:
+//  * interior 256x256 tiles (tile kernel, plus the split kernel for the
+//    last partial round) when N and padded M are multiples of 256,
+//    K >= 512, N <= 2^21 and there are at least 64 tiles;
+//  * 256x256 edge-capable kernel when tiles cross N or padded M but there are
+//    still >= 256 of them;
+//  * 128x128 tiles when that gives >= 256 tiles;
+//  * 64x32 tiles otherwise (small M, few tiles).
+GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed) {
     const int mp = (int)((m + 15u) & ~15u);
-    int kind = kSmall;
-    for (int c = kLarge; c <= kMedium; ++c) {
-        const int tiles = ceil_div(mp, kKinds[c].bm) * ceil_div((int)n, kKinds[c].bn);
-        if (mp >= kKinds[c].bm && tiles >= 256) {
-            kind = c;
-            break;
+    GemmPlan p = {};
+    const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
+    if (mp % 256 == 0 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
+        p.kind = kTiles;
+        p.G = cus;
+        const int tiles_m = mp / 256;
+        p.R = t256 / cus;
+        // the whole-tile rounds must be whole n-columns of tiles
+        if ((p.R * cus) % tiles_m != 0) p.R = 0;
+        p.rem = t256 - p.R * cus;
+        p.s = 1;
+        const int pairs = (int)(k / 256u);
+        const int per_xcd = ceil_div(p.rem, kXcds);
+        if (p.rem > 0 && p.rem <= cus && split_allowed) {
+            int s = (cus / kXcds) / per_xcd;
+            s = s < 1 ? 1 : (s > 4 ? 4 : s);
+            p.s = s > pairs / 2 ? pairs / 2 : s;  // chunks of >= 2 pairs (>= 4 K-steps)
         }
+        if (p.s > 1) {
+            p.workgroups = p.R * cus;
+            p.split_workgroups = kXcds * per_xcd * p.s;
+            p.ws_bytes = split_counter_bytes(p.rem) + (size_t)p.rem * p.s * 256 * 256 * sizeof(float);
+        } else {  // every tile whole
+            p.R = t256 / cus;
+            p.rem = 0;
+            p.workgroups = t256;
+        }
+    } else if (t256 >= 256) {
+        p.kind = kLargeEdge;
+    } else if (mp >= 128 && ceil_div(mp, 128) * ceil_div((int)n, 128) >= 256) {
+        p.kind = kMedium;
+    } else {
+        p.kind = kSmall;
     }
-    GemmPlan p;
-    p.kind = kind;
-    p.bn = kKinds[kind].bn;
-    p.bm = kKinds[kind].bm;
-    p.threads = kKinds[kind].threads;
-    p.workgroups = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
+    p.bn = kKinds[p.kind].bn;
+    p.bm = kKinds[p.kind].bm;
+    p.threads = kKinds[p.kind].threads;
+    if (p.kind != kTiles) p.workgroups = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
     return p;
 }
 
 hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
-                       uint32_t k, const float* act_scale, float w_scale, float* y,
-                       hipStream_t st) {
-    const GemmPlan p = plan_gemm(m, n, k);
+                       uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
+                       size_t ws_bytes, int cus, hipStream_t st) {
+    GemmPlan p = plan_gemm(m, n, k, cus, true);
+    if (p.kind == kTiles && p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
+        p = plan_gemm(m, n, k, cus, false);  // no room for partial sums: whole tiles only
     const int mp = (int)((m + 15u) & ~15u);
     const int tiles_m = ceil_div(mp, p.bm), tiles_n = ceil_div((int)n, p.bn);
     const int group_m = tiles_m < 8 ? tiles_m : 8;
     switch (p.kind) {
-        case kLarge:
-            if ((n % 256u) == 0 && (mp % 256) == 0)  // every tile interior: pipelined kernel
-                fp8_gemm_pipe_kernel<<<p.workgroups, p.threads, 0, st>>>(
-                    a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n,
-                    group_m);
-            else
-                fp8_gemm_deep_kernel<256, 256, 2, 2><<<p.workgroups, p.threads, 0, st>>>(
-                    a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n,
-                    group_m);
+        case kTiles: {
+            // whole tiles: the first n-columns (all of them without a split)
+            const int nd = p.workgroups / tiles_m;
+            if (p.workgroups > 0)
+                fp8_gemm_tile_kernel<<<p.workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale,
+                                                                   w_scale, tiles_m, nd, group_m);
+            if (p.s > 1) {
+                SplitPlan sp;
+                sp.tiles_m = tiles_m;
+                sp.nd = nd;
+                sp.rem = p.rem;
+                sp.per_xcd = ceil_div(p.rem, kXcds);
+                // groups of ~sqrt(tiles per XCD) m-tiles: each XCD's block of tiles is near square
+                int tgm = 1;
+                while (tgm * 2 <= tiles_m && tgm * tgm * 4 <= sp.per_xcd) tgm *= 2;
+                sp.tail_gm = tgm;
+                sp.s = p.s;
+                sp.pairs = (int)(k / 256u);
+                unsigned* cnt = static_cast<unsigned*>(ws);
+                float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem));
+                fp8_gemm_split_kernel<<<p.split_workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k,
+                                                                          act_scale, w_scale, sp, part, cnt);
+            }
+            (void)tiles_n;
+            break;
+        }
+        case kLargeEdge:
+            fp8_gemm_deep_kernel<256, 256, 2, 2><<<p.workgroups, p.threads, 0, st>>>(
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
             break;
         case kMedium:
             fp8_gemm_deep_kernel<128, 128, 2, 2><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n,
-                group_m);
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
             break;
         default:
             fp8_gemm_kernel<64, 32, 2, 1><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n,
-                group_m);
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
             break;
     }
     return hipGetLastError();

@@ -33,10 +33,14 @@ hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hi
 // ---- gemm.hip
 struct GemmPlan {
     int bn, bm, threads, workgroups, kind;
+    // interior-tile plan: CUs, whole-tile rounds, split tiles, K chunks per
+    // split tile, workgroups of the split kernel
+    int G, R, rem, s, split_workgroups;
+    size_t ws_bytes;  // workspace the plan needs (0: none)
 };
-GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k);
+GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed);
 hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
-                       uint32_t k, const float* act_scale, float w_scale, float* y,
-                       hipStream_t st);
+                       uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
+                       size_t ws_bytes, int cus, hipStream_t st);
 
 }  // namespace rz

@@ -124,13 +124,25 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
  *   act_scale_dev device, float[2] from rz_fp8_quant_act
  *   w_scale       the host scale from rz_fp8_pack_weight
  *   y             device out, fp32 [m][n] row-major (only rows < m written)
- * Products are accumulated in fp32 on the matrix cores (no fp16 stage).
+ *   ws, ws_bytes  optional device workspace (may be NULL / 0) of at least
+ *                 rz_fp8_gemm_workspace_bytes(m, n, k) bytes, zero-filled
+ *                 before its first use; every call leaves it reusable.  It
+ *                 holds partial sums when the last round of output tiles is
+ *                 split along K to keep every compute unit busy; without it
+ *                 (or when it is too small) that round runs unsplit.  Calls
+ *                 that share a workspace must be ordered (same stream).
+ * Products are accumulated in fp32 on the matrix cores (no fp16 stage); the
+ * summation order may differ between calls with and without a workspace.
  * k <= RZ_MAX_GEMM_K.  m == 0 or n == 0 is a no-op (any pointer may then
  * be NULL).
  */
 int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                 uint32_t k, const float* act_scale_dev, float w_scale, float* y,
-                void* stream);
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace rz_fp8_gemm can use for this shape on the current device
+ * (0 when it would not split). */
+size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k);
 
 /* ---------------------------------------------------------------------
  * Diagnostics: the individual steps, exposed so that each can be checked
@@ -161,8 +173,10 @@ int rz_e4m3_encode(const float* x, uint64_t count, float scale, uint8_t* out,
 int rz_fp8_scales(const float* absmax_dev, uint64_t count, float* q_out_dev,
                   float* dq_out_dev, void* stream);
 
-/* GEMM tile configuration rz_fp8_gemm would launch for this shape:
- * writes {BN, BM, threads, workgroups} to cfg_out[4] (host). */
+/* GEMM tile configuration rz_fp8_gemm would launch for this shape (with a
+ * large enough workspace): writes {BN, BM, threads, workgroups} to
+ * cfg_out[4] (host); workgroups counts every launch of the call (whole
+ * tiles plus K chunks of split tiles). */
 int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out);
 
 const char* rz_status_string(int status);

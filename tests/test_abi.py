@@ -92,24 +92,35 @@ def test_quant_act_validation(L):
 
 
 def test_gemm_validation(L):
-    f = L.rz_fp8_gemm
-    assert f(None, P2, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_NULL
-    assert f(P, None, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_NULL
-    assert f(P, P2, 4, 8, 256, None, 1.0, P, None) == RZ_ERR_NULL
-    assert f(P, P2, 4, 8, 256, P3, 1.0, None, None) == RZ_ERR_NULL
-    assert f(P, P2, 4, 8, 255, P3, 1.0, P, None) == RZ_ERR_SHAPE
-    assert f(P, P2, 4, 8, 0, P3, 1.0, P, None) == RZ_ERR_SHAPE
-    assert f(P, P2, 4, 8, 1 << 24, P3, 1.0, P, None) == RZ_ERR_SHAPE
-    assert f(P, P2, 1 << 20, 1 << 20, 256, P3, 1.0, P, None) == RZ_ERR_SHAPE
-    assert f(BAD, P2, 4, 8, 256, P3, 1.0, P, None) == RZ_ERR_ALIGN
-    assert f(P, P2, 4, 8, 256, P3, 1.0, BAD, None) == RZ_ERR_ALIGN
-    assert f(P, P2, 4, 8, 256, P3, float("nan"), P, None) == RZ_ERR_VALUE
-    assert f(P, P2, 4, 8, 256, P3, float("inf"), P, None) == RZ_ERR_VALUE
+    def f(a, w, m, n, k, sc, ws_, y, ws=None, wsb=0):
+        return L.rz_fp8_gemm(a, w, m, n, k, sc, ws_, y, ws, wsb, None)
+    assert f(None, P2, 4, 8, 256, P3, 1.0, P) == RZ_ERR_NULL
+    assert f(P, None, 4, 8, 256, P3, 1.0, P) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 256, None, 1.0, P) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 256, P3, 1.0, None) == RZ_ERR_NULL
+    assert f(P, P2, 4, 8, 255, P3, 1.0, P) == RZ_ERR_SHAPE
+    assert f(P, P2, 4, 8, 0, P3, 1.0, P) == RZ_ERR_SHAPE
+    assert f(P, P2, 4, 8, 1 << 24, P3, 1.0, P) == RZ_ERR_SHAPE
+    assert f(P, P2, 1 << 20, 1 << 20, 256, P3, 1.0, P) == RZ_ERR_SHAPE
+    assert f(BAD, P2, 4, 8, 256, P3, 1.0, P) == RZ_ERR_ALIGN
+    assert f(P, P2, 4, 8, 256, P3, 1.0, BAD) == RZ_ERR_ALIGN
+    assert f(P, P2, 4, 8, 256, P3, 1.0, P, BAD, 1024) == RZ_ERR_ALIGN
+    assert f(P, P2, 4, 8, 256, P3, float("nan"), P) == RZ_ERR_VALUE
+    assert f(P, P2, 4, 8, 256, P3, float("inf"), P) == RZ_ERR_VALUE
     # empty products are no-ops that touch nothing (no device needed)
-    assert f(P, P2, 0, 8, 256, P3, 1.0, P, None) == RZ_OK
-    assert f(P, P2, 4, 0, 256, P3, 1.0, P, None) == RZ_OK
-    assert f(None, None, 0, 8, 256, None, 1.0, None, None) == RZ_OK
-    assert f(None, None, 0, 8, 255, None, 1.0, None, None) == RZ_ERR_SHAPE
+    assert f(P, P2, 0, 8, 256, P3, 1.0, P) == RZ_OK
+    assert f(P, P2, 4, 0, 256, P3, 1.0, P) == RZ_OK
+    assert f(None, None, 0, 8, 256, None, 1.0, None) == RZ_OK
+    assert f(None, None, 0, 8, 255, None, 1.0, None) == RZ_ERR_SHAPE
+
+
+def test_gemm_workspace_sizes(L):
+    # split-K workspace only for persistent plans whose last round is split
+    assert L.rz_fp8_gemm_workspace_bytes(16, 256, 512) == 0
+    assert L.rz_fp8_gemm_workspace_bytes(0, 256, 512) == 0
+    assert L.rz_fp8_gemm_workspace_bytes(2048, 256, 300) == 0
+    big = L.rz_fp8_gemm_workspace_bytes(2048, 18944, 3584)
+    assert big > 0 and big % 16 == 0
 
 
 def test_diagnostics_validation(L):
@@ -137,8 +148,34 @@ def test_plans_cover_shapes(L):
                     (2048, 3584, 18944), (4096, 18944, 3584), (1, 4608, 3584), (1000, 4608, 3584)]:
         bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
         mp = rz.rz_pad_m(m)
-        assert wgs == -(-mp // bm) * -(-n // bn)
+        tiles = -(-mp // bm) * -(-n // bn)
+        interior = (bn, bm) == (256, 256) and mp % 256 == 0 and n % 256 == 0 and k >= 512 and tiles >= 64
+        assert wgs == (_interior_wgs(mp // 256, n // 256, k) if interior else tiles)
         assert threads in (64, 128, 256, 512)
+
+
+def _interior_wgs(tiles_m, tiles_n, k, cus=256):
+    """Workgroups of an interior-tile plan (256 CUs without a device): whole
+    tiles for the full rounds, then the leftover tiles split along K into s
+    chunks per tile (s*leftover <= CUs, chunks of >= 2 K pairs), or every
+    tile whole when no split fits."""
+    t = tiles_m * tiles_n
+    r = t // cus
+    if (r * cus) % tiles_m:
+        r = 0
+    rem = t - r * cus
+    per_xcd = -(-rem // 8)
+    s = min(4, max(1, (cus // 8) // per_xcd), (k // 256) // 2) if 0 < rem <= cus else 1
+    return r * cus + 8 * per_xcd * s if s > 1 else t
+
+
+def test_interior_plan_examples(L):
+    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles in 3 K chunks
+    assert rz.rz_fp8_gemm_plan(2048, 18944, 3584)[3] == 512 + 240
+    # FFN down at M=2048: 112 tiles, all split in 2 K chunks
+    assert rz.rz_fp8_gemm_plan(2048, 3584, 18944)[3] == 224
+    # M=4096: 1184 tiles, 160 left over is too many to split: all whole
+    assert rz.rz_fp8_gemm_plan(4096, 18944, 3584)[3] == 1184
 
 
 def test_binding_refuses_host_tensors(L):

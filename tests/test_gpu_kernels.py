@@ -259,6 +259,41 @@ def test_gemm_large_plan_full(rz):
     check_gemm(y, a8, w8, m, sc[1], np.float32(0.25))
 
 
+def _codes(g, shape):
+    a = g.integers(0, 0x7F, size=shape).astype(np.uint8)
+    return a | (g.integers(0, 2, size=shape) << 7).astype(np.uint8)
+
+
+@pytest.mark.parametrize("m,n,k,full", [
+    (2048, 2560, 1536, True),    # 80 tiles: all split in 3 K chunks of 2 pairs
+    (2048, 2560, 2816, False),   # 80 tiles in 3 uneven chunks (3, 4, 4 pairs)
+    (2048, 2560, 768, True),     # 80 tiles, K too short to split: whole tiles
+    (2048, 3584, 1024, True),    # 112 tiles: all split in 2
+    (2048, 10240, 1024, False),  # 320 tiles: one whole round + 64 tiles split in 2
+    (4096, 4096, 512, False),    # 256 tiles: exactly one round
+])
+def test_gemm_interior_plans(rz, m, n, k, full):
+    bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+    assert (bn, bm, threads) == (256, 256, 256)
+    g = np.random.Generator(np.random.PCG64(m + n + k))
+    a8, w8 = _codes(g, (m, k)), _codes(g, (n, k))
+    sc = np.array([1.0, 0.03, 0, 0], np.float32)
+    wdq = np.float32(0.011)
+    A, Wd, S = dev(a8), dev(w8), dev(sc)
+    rows = np.arange(m) if full else np.unique(np.concatenate([[0, 1, m - 1], g.choice(m, 61, replace=False)]))
+    yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
+    need = rz.rz_fp8_gemm_workspace_bytes(m, n, k)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    # with the workspace (split tail) twice in a row, then without (whole tiles)
+    for use_ws in (ws, ws, None):
+        y = host(rz.rz_fp8_gemm(A, Wd, m, S, float(wdq), ws=use_ws))
+        err = np.abs(y[rows].astype(np.float64) - yr)
+        assert (err <= tol).all(), f"{(err > tol).sum()} out of bound (ws={use_ws is not None})"
+    if need:
+        tiles = (m // 256) * (n // 256)
+        assert (host(ws[:4 * (tiles % 256)]) == 0).all()  # arrival counters left at zero
+
+
 def test_gemm_identity_weight(rz):
     k, n, m = 512, 64, 37
     w8 = np.zeros((n, k), np.uint8)
