@@ -229,16 +229,17 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][4], const uint8_t* cur, uin
 //
 // When padded M and N are multiples of 256 the output splits into T whole
 // tiles.  G = one workgroup per CU; the first R*G tiles (R = floor(T/G) full
-// rounds, chosen as whole n-columns of tiles) run one tile per workgroup in
-// fp8_gemm_tile_kernel.  The rem = T - R*G tiles left over would leave most
-// CUs idle for a whole tile time, so fp8_gemm_split_kernel splits each of
-// them along K into s chunks (s*rem <= G) that run in parallel; the chunks
-// store partial sums in a workspace and count themselves in, and the last to
-// arrive adds the s partials in chunk order (so the result does not depend on
-// the arrival order) and writes the output.  No workgroup waits for another.
+// rounds, chosen as whole n-columns of tiles) run one tile per workgroup.
+// The rem = T - R*G tiles left over would leave most CUs idle for a whole
+// tile time, so each of them is split along K into s chunks (s*rem <= G)
+// that run in parallel, as workgroups after the whole tiles in the same
+// launch; the chunks store partial sums in a workspace, and the last chunk
+// of a tile to finish adds the s partial sums in chunk order (so the result
+// does not depend on the arrival order) and writes the output.  No
+// workgroup waits for another.
 //
-// Both kernels run the same K loop (tile_mainloop): two LDS slots, the global
-// loads three K-steps ahead of the MFMAs in two register sets.
+// The K loop (tile_mainloop): two LDS slots, the global loads three K-steps
+// ahead of the MFMAs in two register sets.
 // ---------------------------------------------------------------------------
 
 // Origin of tile t in the grouped order of a tiles_m x tiles_n region
@@ -302,11 +303,12 @@ __device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][4], uint8_t (&smem)
     }
 }
 
-// acc * scale -> the tile's rows of Y (float4 runs of n).  `yrs` covers the
-// tile's valid rows only, so the stores of rows m >= M fall outside the
+// acc * mul -> a 256x256 fp32 tile at byte offset 4*(row*stride + nb + col)
+// of `rs` (float4 runs of the output column).  For the output, `rs` covers
+// the tile's valid rows only, so the stores of rows m >= M fall outside the
 // buffer range and are dropped by the hardware (no branches).
-__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t yrs, int N, int n0,
-                                           int wn, int wm, int lane, float scale) {
+__device__ __forceinline__ void store_acc(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t rs, uint32_t stride,
+                                          uint32_t nb, int wn, int wm, int lane, float mul) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -314,11 +316,11 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], __amdgpu_buf
             const uint32_t row = (uint32_t)(wm * 128 + j * 32 + (lane & 31));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t n = (uint32_t)(n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
-                const float4 v = make_float4(acc[i][j][4 * q] * scale, acc[i][j][4 * q + 1] * scale,
-                                             acc[i][j][4 * q + 2] * scale, acc[i][j][4 * q + 3] * scale);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yrs,
-                                                       (row * (uint32_t)N + n) * 4u, 0, 0);
+                const uint32_t col = nb + (uint32_t)(wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
+                const float4 v = make_float4(acc[i][j][4 * q] * mul, acc[i][j][4 * q + 1] * mul,
+                                             acc[i][j][4 * q + 2] * mul, acc[i][j][4 * q + 3] * mul);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (row * stride + col) * 4u, 0,
+                                                       0);
             }
         }
     }
@@ -330,56 +332,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
     return __builtin_amdgcn_make_buffer_rsrc(Y + (size_t)m0 * N, (short)0, rows * N * 4, 0x00020000);
 }
 
-// One interior tile per workgroup over the first T tiles of the grouped
-// order (T = gridDim.x).  The dispatcher sends workgroup w to XCD w % 8, so
-// XCD x is given the contiguous range of tiles [x*T/8, (x+1)*T/8): the
-// workgroups that run together on one XCD share weight and activation rows
-// through its L2.
-__global__ __launch_bounds__(256) void fp8_gemm_tile_kernel(const uint8_t* __restrict__ A,
-                                                            const uint8_t* __restrict__ Wt, float* __restrict__ Y,
-                                                            int M, int N, int K, const float* __restrict__ act_scale,
-                                                            float w_scale, int tiles_m, int tiles_n, int group_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
-    const int T = (int)gridDim.x;
-    const int w = blockIdx.x;
-    const int tall = T / kXcds, rem = T % kXcds;
-    const int x = w % kXcds, loc = w / kXcds;
-    const int t = x * tall + (x < rem ? x : rem) + loc;
-    int n0, m0;
-    grouped_origin(t, tiles_m, tiles_n, group_m, n0, m0);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int wn = wid & 1, wm = wid >> 1;
-    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
-    const PipeOffsets po = pipe_offsets(tid, wn, wm, lane);
-
-    v16f acc[4][4];
-    tile_mainloop(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
-                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, 0, K / kBK, po);
-    store_tile(acc, tile_out_rsrc(Y, M, N, m0), N, n0, wn, wm, lane, act_scale[1] * w_scale);
-}
-
-// Split tiles: the n-columns [nd, tiles_n) of tiles (all m), rem tiles in a
-// grouped order with groups of tail_gm m-tiles.  XCD x owns the tiles
-// [x*per_xcd, (x+1)*per_xcd) and its workgroups take them chunk by chunk, so
-// all s chunks of a tile run on one XCD, whose L2 is coherent for its CUs.
-// Chunk c covers the 256-byte K pairs [c*pairs/s, (c+1)*pairs/s).
-struct SplitPlan {
-    int tiles_m, nd, rem, tail_gm, per_xcd, s, pairs;
+// Work of the interior-tile kernel.  The grid is nwhole whole-tile
+// workgroups followed by the K chunks of the split tiles.
+//   Whole tiles: the first nd n-columns of tiles (all m), in the grouped
+//   order (groups of group_m m-tiles).  The dispatcher sends workgroup w to
+//   XCD w % 8, so XCD x is given the contiguous range [x*T/8, (x+1)*T/8) of
+//   that order: the workgroups that run together on one XCD share weight
+//   and activation rows through its L2.
+//   Split tiles: n-columns [nd, tiles_n), rem tiles in a grouped order with
+//   groups of tail_gm m-tiles.  XCD x owns the tiles [x*per_xcd,
+//   (x+1)*per_xcd) and its workgroups take them chunk by chunk, so the s
+//   chunks of a tile run on one XCD, whose L2 is coherent for its CUs.
+//   Chunk c covers the 256-byte K pairs [c*pairs/s, (c+1)*pairs/s).
+struct InteriorPlan {
+    int tiles_m, nd, nwhole, group_m;
+    int rem, tail_gm, per_xcd, s, pairs;
 };
 
-// Last arriver of a split tile: out = sum over chunks c = 0..S-1 (in that
-// order) of partial c, scaled.  Partials are thread-major float4 blocks:
-// block b = (i*4 + j)*4 + q of thread t at float offset (b*256 + t)*4.
-// NB blocks are loaded per batch (NB*S loads in flight per thread).
+// Split-tile epilogue, after the chunk has stored its partial sum (a
+// 256x256 fp32 tile, row stride 256) in its slot: wait until the stores
+// have reached the XCD's L2 and count in.  The last chunk to arrive resets
+// the counter, adds the s partial sums in chunk order, scales, and writes
+// the output: float4 f of the tile (row f/64, columns 4*(f%64)..+3), 64
+// per thread, NB at a time (NB*S loads in flight per thread).
 template <int S, int NB>
-__device__ __forceinline__ void fixup_tile(const float* __restrict__ parts, __amdgpu_buffer_rsrc_t yrs, int N,
-                                           int n0, int wn, int wm, int lane, int tid, float scale) {
+__device__ __forceinline__ void split_finish(const float* __restrict__ parts, unsigned* arr, unsigned& arrival,
+                                             __amdgpu_buffer_rsrc_t yrs, int N, int n0, int tid, float scale) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) arrival = __hip_atomic_fetch_add(arr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != (unsigned)(S - 1)) return;
+    if (tid == 0) __hip_atomic_store(arr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
     const __amdgpu_buffer_rsrc_t prs =
         tile_rsrc(reinterpret_cast<const uint8_t*>(parts), (uint32_t)S * 256u * 256u * 4u);
-    for (int b0 = 0; b0 < 64; b0 += NB) {
+    for (int f0 = 0; f0 < 64; f0 += NB) {
         u32x4 v[S][NB];
 #pragma unroll
         for (int c = 0; c < S; ++c)
@@ -387,47 +374,53 @@ __device__ __forceinline__ void fixup_tile(const float* __restrict__ parts, __am
             for (int u = 0; u < NB; ++u)  // sc0: not from this CU's L1
                 v[c][u] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               prs, ((uint32_t)c * 65536u + (uint32_t)((b0 + u) * 256 + tid) * 4u) * 4u, 0, 1));
+                               prs, ((uint32_t)c * 65536u + (uint32_t)((f0 + u) * 256 + tid) * 4u) * 4u, 0, 1));
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const int b = b0 + u;
-            const int i = b >> 4, j = (b >> 2) & 3, q = b & 3;
-            float4 sum = make_float4(__uint_as_float(v[0][u].x), __uint_as_float(v[0][u].y),
-                                     __uint_as_float(v[0][u].z), __uint_as_float(v[0][u].w));
+            const uint32_t f = (uint32_t)((f0 + u) * 256 + tid);
+            float r[4];
 #pragma unroll
-            for (int c = 1; c < S; ++c) {
-                sum.x += __uint_as_float(v[c][u].x);
-                sum.y += __uint_as_float(v[c][u].y);
-                sum.z += __uint_as_float(v[c][u].z);
-                sum.w += __uint_as_float(v[c][u].w);
+            for (int e = 0; e < 4; ++e) {
+                float sum = __uint_as_float(v[0][u][e]);
+#pragma unroll
+                for (int c = 1; c < S; ++c) sum += __uint_as_float(v[c][u][e]);
+                r[e] = sum * scale;
             }
-            const uint32_t row = (uint32_t)(wm * 128 + j * 32 + (lane & 31));
-            const uint32_t n = (uint32_t)(n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
-            const float4 o = make_float4(sum.x * scale, sum.y * scale, sum.z * scale, sum.w * scale);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), yrs, (row * (uint32_t)N + n) * 4u, 0,
-                                                   0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, make_float4(r[0], r[1], r[2], r[3])), yrs,
+                                                   ((f >> 6) * (uint32_t)N + (uint32_t)n0 + 4u * (f & 63u)) * 4u, 0, 0);
         }
     }
 }
 
-__global__ __launch_bounds__(256) void fp8_gemm_split_kernel(
+__global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M, int N, int K,
-    const float* __restrict__ act_scale, float w_scale, SplitPlan P, float* __restrict__ part,
+    const float* __restrict__ act_scale, float w_scale, InteriorPlan P, float* __restrict__ part,
     unsigned* __restrict__ cnt) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
     __shared__ unsigned arrival;
 
-    const int g = blockIdx.x;
-    const int x = g % kXcds, j = g / kXcds;
-    const int base = x * P.per_xcd;
-    int count = P.rem - base;
-    count = count < P.per_xcd ? count : P.per_xcd;
-    if (count <= 0 || j >= count * P.s) return;
-    const int tl = base + j / P.s, chunk = j % P.s;
-    int n0, m0;
-    grouped_origin(tl, P.tiles_m, (N >> 8) - P.nd, P.tail_gm, n0, m0);
-    n0 += P.nd * 256;
-    const int p0 = chunk * P.pairs / P.s, p1 = (chunk + 1) * P.pairs / P.s;
+    const int bid = blockIdx.x;
+    int n0, m0, k0 = 0, KS = K / kBK, tl = -1, chunk = 0;
+    if (bid < P.nwhole) {
+        const int T = P.nwhole;
+        const int tall = T / kXcds, rem = T % kXcds;
+        const int x = bid % kXcds, loc = bid / kXcds;
+        grouped_origin(x * tall + (x < rem ? x : rem) + loc, P.tiles_m, P.nd, P.group_m, n0, m0);
+    } else {
+        const int g = bid - P.nwhole;  // nwhole is a multiple of 8: same XCD
+        const int x = g % kXcds, j = g / kXcds;
+        const int base = x * P.per_xcd;
+        int count = P.rem - base;
+        count = count < P.per_xcd ? count : P.per_xcd;
+        if (count <= 0 || j >= count * P.s) return;
+        tl = base + j / P.s;
+        chunk = j % P.s;
+        grouped_origin(tl, P.tiles_m, (N >> 8) - P.nd, P.tail_gm, n0, m0);
+        n0 += P.nd * 256;
+        const int p0 = chunk * P.pairs / P.s, p1 = (chunk + 1) * P.pairs / P.s;
+        k0 = 2 * p0;
+        KS = 2 * (p1 - p0);
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -438,35 +431,21 @@ __global__ __launch_bounds__(256) void fp8_gemm_split_kernel(
 
     v16f acc[4][4];
     tile_mainloop(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
-                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, 2 * p0, 2 * (p1 - p0),
-                  po);
-
-    float* parts = part + (size_t)tl * P.s * (256 * 256);
-    float* mine = parts + (size_t)chunk * (256 * 256);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4*>(mine + ((size_t)(((i * 4 + jj) * 4 + q) * 256 + tid) << 2)) =
-                    make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
-                                acc[i][jj][4 * q + 3]);
-    // All chunks of this tile run on this XCD, whose L2 is coherent for its
-    // CUs: wait until the stores have reached it, then count in.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) arrival = __hip_atomic_fetch_add(cnt + tl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != (unsigned)(P.s - 1)) return;
-    if (tid == 0)  // ready the counter for the next call
-        __hip_atomic_store(cnt + tl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, k0, KS, po);
     const __amdgpu_buffer_rsrc_t yrs = tile_out_rsrc(Y, M, N, m0);
     const float scale = act_scale[1] * w_scale;
+    // One store for both kinds of work: a whole tile writes acc*scale to Y;
+    // a K chunk writes acc (times 1, exact) to its partial slot.
+    float* parts = tl < 0 ? nullptr : part + (size_t)tl * P.s * (256 * 256);
+    const __amdgpu_buffer_rsrc_t srs =
+        tl < 0 ? yrs : tile_rsrc(reinterpret_cast<const uint8_t*>(parts + (size_t)chunk * (256 * 256)), 256u * 256u * 4u);
+    store_acc(acc, srs, tl < 0 ? (uint32_t)N : 256u, tl < 0 ? (uint32_t)n0 : 0u, wn, wm, lane, tl < 0 ? scale : 1.0f);
+    if (tl < 0) return;
+    unsigned* arr = cnt + tl;  // arrival counters [0, rem); partial slots follow
     switch (P.s) {
-        case 2: fixup_tile<2, 16>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
-        case 3: fixup_tile<3, 16>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
-        default: fixup_tile<4, 8>(parts, yrs, N, n0, wn, wm, lane, tid, scale); break;
+        case 2: split_finish<2, 16>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
+        case 3: split_finish<3, 16>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
+        default: split_finish<4, 8>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
     }
 }
 
@@ -762,28 +741,25 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     const int group_m = tiles_m < 8 ? tiles_m : 8;
     switch (p.kind) {
         case kTiles: {
-            // whole tiles: the first n-columns (all of them without a split)
-            const int nd = p.workgroups / tiles_m;
-            if (p.workgroups > 0)
-                fp8_gemm_tile_kernel<<<p.workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale,
-                                                                   w_scale, tiles_m, nd, group_m);
-            if (p.s > 1) {
-                SplitPlan sp;
-                sp.tiles_m = tiles_m;
-                sp.nd = nd;
-                sp.rem = p.rem;
-                sp.per_xcd = ceil_div(p.rem, kXcds);
-                // groups of ~sqrt(tiles per XCD) m-tiles: each XCD's block of tiles is near square
-                int tgm = 1;
-                while (tgm * 2 <= tiles_m && tgm * tgm * 4 <= sp.per_xcd) tgm *= 2;
-                sp.tail_gm = tgm;
-                sp.s = p.s;
-                sp.pairs = (int)(k / 256u);
-                unsigned* cnt = static_cast<unsigned*>(ws);
-                float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem));
-                fp8_gemm_split_kernel<<<p.split_workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k,
-                                                                          act_scale, w_scale, sp, part, cnt);
-            }
+            InteriorPlan ip;
+            ip.tiles_m = tiles_m;
+            ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without a split)
+            ip.nd = p.workgroups / tiles_m;
+            ip.group_m = group_m;
+            ip.rem = p.s > 1 ? p.rem : 0;
+            ip.per_xcd = ceil_div(ip.rem, kXcds);
+            // groups of ~sqrt(tiles per XCD) m-tiles: each XCD's block of split tiles is near square
+            int tgm = 1;
+            while (tgm * 2 <= tiles_m && tgm * tgm * 4 <= ip.per_xcd) tgm *= 2;
+            ip.tail_gm = tgm;
+            ip.s = p.s;
+            ip.pairs = (int)(k / 256u);
+            unsigned* cnt = p.s > 1 ? static_cast<unsigned*>(ws) : nullptr;
+            float* part = p.s > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem))
+                                  : nullptr;
+            const int grid = p.workgroups + (p.s > 1 ? p.split_workgroups : 0);
+            fp8_gemm_interior_kernel<<<grid, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale, w_scale,
+                                                           ip, part, cnt);
             (void)tiles_n;
             break;
         }

@@ -290,8 +290,8 @@ def test_gemm_interior_plans(rz, m, n, k, full):
         err = np.abs(y[rows].astype(np.float64) - yr)
         assert (err <= tol).all(), f"{(err > tol).sum()} out of bound (ws={use_ws is not None})"
     if need:
-        tiles = (m // 256) * (n // 256)
-        assert (host(ws[:4 * (tiles % 256)]) == 0).all()  # arrival counters left at zero
+        rem = (m // 256) * (n // 256) % 256
+        assert (host(ws[:4 * rem]) == 0).all()  # arrival counters left at zero for the next call
 
 
 def test_gemm_identity_weight(rz):
