@@ -21,44 +21,41 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Pass 1 over fp32 data: per-workgroup max key.  x is 16-byte aligned; the
-// last count % 4 elements are read one at a time by workgroup 0.
+// Pass 1 over fp32 data: per-workgroup max key.  x is 16-byte aligned.
+// Each workgroup iteration covers kU*kThreads consecutive float4 (thread t
+// reads t, t + kThreads, ...), all issued before any is used, so every thread
+// keeps kU loads in flight.  The last count % 4 elements are read one at a
+// time by workgroup 0.
+constexpr int kU = 8;
 __global__ __launch_bounds__(kThreads) void absmax_partial_kernel(const float* __restrict__ x,
                                                                   uint64_t count,
                                                                   uint32_t* __restrict__ partial) {
     __shared__ uint32_t red[kThreads / kWave];
     const float4* x4 = reinterpret_cast<const float4*>(x);
     const uint64_t n4 = count >> 2;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    uint32_t k0 = 0, k1 = 0;
-    uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    // two loads in flight per iteration
-    for (; i + stride < n4; i += 2 * stride) {
-        const float4 a = x4[i];
-        const float4 b = x4[i + stride];
-        uint32_t t;
-        t = abs_key(a.x); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.y); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.z); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.w); k0 = k0 > t ? k0 : t;
-        t = abs_key(b.x); k1 = k1 > t ? k1 : t;
-        t = abs_key(b.y); k1 = k1 > t ? k1 : t;
-        t = abs_key(b.z); k1 = k1 > t ? k1 : t;
-        t = abs_key(b.w); k1 = k1 > t ? k1 : t;
-    }
-    if (i < n4) {
-        const float4 a = x4[i];
-        uint32_t t;
-        t = abs_key(a.x); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.y); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.z); k0 = k0 > t ? k0 : t;
-        t = abs_key(a.w); k0 = k0 > t ? k0 : t;
+    const uint64_t step = (uint64_t)gridDim.x * kThreads * kU;
+    uint32_t k = 0;
+    for (uint64_t i0 = (uint64_t)blockIdx.x * kThreads * kU + threadIdx.x; i0 < n4; i0 += step) {
+        float4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const uint64_t i = i0 + (uint64_t)u * kThreads;
+            v[u] = i < n4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            uint32_t t;
+            t = abs_key(v[u].x); k = k > t ? k : t;
+            t = abs_key(v[u].y); k = k > t ? k : t;
+            t = abs_key(v[u].z); k = k > t ? k : t;
+            t = abs_key(v[u].w); k = k > t ? k : t;
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x < (count & 3)) {
         const uint32_t t = abs_key(x[(n4 << 2) + threadIdx.x]);
-        k0 = k0 > t ? k0 : t;
+        k = k > t ? k : t;
     }
-    uint32_t key = block_max_u32<kThreads>(k0 > k1 ? k0 : k1, red);
+    const uint32_t key = block_max_u32<kThreads>(k, red);
     if (threadIdx.x == 0) partial[blockIdx.x] = key;
 }
 
@@ -89,10 +86,7 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(
                 const float4 a = x4[4 * g + j];
                 v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
             }
-            uint32_t c[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) c[j] = e4m3_scaled(v[j], q);
-            o16[g] = pack16(c);
+            o16[g] = e4m3_scaled16(v, q);
         } else {
             o16[g] = make_uint4(0u, 0u, 0u, 0u);
         }
@@ -121,10 +115,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
             const float4 a = x4[4 * g + j];
             v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
         }
-        uint32_t c[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) c[j] = e4m3_scaled(v[j], q);
-        reinterpret_cast<uint4*>(out)[g] = pack16(c);
+        reinterpret_cast<uint4*>(out)[g] = e4m3_scaled16(v, q);
     }
     const uint64_t tail = count & 15;
     if (tid < tail) {
@@ -151,9 +142,9 @@ int grid_for(uint64_t work_items, int cap) {
     return (int)(g > (uint64_t)cap ? (uint64_t)cap : g);
 }
 
-// Partial workgroups for an absmax over `count` floats: about 8 float4 per
-// thread, at most kMaxPartials.
-int absmax_groups(uint64_t count) { return grid_for(((count >> 2) + 7) / 8, kMaxPartials); }
+// Partial workgroups for an absmax over `count` floats: at least one
+// iteration of kU float4 per thread, at most kMaxPartials.
+int absmax_groups(uint64_t count) { return grid_for(((count >> 2) + kU - 1) / kU, kMaxPartials); }
 
 }  // namespace
 

@@ -121,6 +121,28 @@ const char* rz_last_error_string(void) { return g_last_error.c_str(); }
 
 const char* rz_version(void) { return "rz_fp8 0.1.0 gfx950"; }
 
+// Per-thread slot of fine-grained (coherent) pinned host memory that the
+// pack's encode kernel writes the scales into, so the host scale needs no
+// device-to-host copy, only the stream synchronisation.  Allocated on first
+// use, kept until the process ends; null if the allocation fails (then the
+// scales are copied back).  Calls on one thread are sequential (each one
+// synchronises its stream before returning), so one slot per thread is
+// enough.
+static float* host_scale_slot() {
+    thread_local float* slot = nullptr;
+    thread_local bool tried = false;
+    if (!tried) {
+        tried = true;
+        void* p = nullptr;
+        if (hipHostMalloc(&p, 64, hipHostMallocCoherent | hipHostMallocPortable) == hipSuccess) {
+            void* dp = nullptr;
+            if (hipHostGetDevicePointer(&dp, p, 0) == hipSuccess && dp == p) slot = static_cast<float*>(p);
+        }
+        (void)hipGetLastError();  // a failed attempt leaves no error behind
+    }
+    return slot;
+}
+
 int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
                        float* w_scale_host, float* w_absmax_host, void* ws, void* stream) {
     static const char* fn = "rz_fp8_pack_weight";
@@ -134,15 +156,22 @@ int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, ui
     if (int r = check_device(fn)) return r;
     hipStream_t st = as_stream(stream);
     const uint64_t nb = (uint64_t)n * (k / 256u);
+    float* slot = host_scale_slot();
     hipError_t e = rz::launch_pack(qtype, static_cast<const uint8_t*>(blocks), nb, w_fp8,
-                                   static_cast<uint8_t*>(ws), st);
+                                   static_cast<uint8_t*>(ws), slot, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     float sc[4];
-    e = hipMemcpyAsync(sc, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof sc,
-                       hipMemcpyDeviceToHost, st);
-    if (e != hipSuccess) return hip_fail(e, fn);
+    if (!slot) {  // no pinned slot: copy the scales back
+        e = hipMemcpyAsync(sc, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof sc,
+                           hipMemcpyDeviceToHost, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, fn);
+    if (slot) {
+        const volatile float* v = slot;  // written by the device
+        for (int i = 0; i < 4; ++i) sc[i] = v[i];
+    }
     *w_scale_host = sc[2];
     if (w_absmax_host) *w_absmax_host = sc[0];
     return RZ_OK;

@@ -29,25 +29,28 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kQ6Chunk = 64;  // Q6_K blocks staged per workgroup iteration
 
-// Calls f(first_element, vals[16]) for every run of 16 consecutive weights of
-// the tensor, in an order that keeps each wave on contiguous memory.
+// Calls unit(...) for every decode unit of the tensor, in an order that keeps
+// each wave on contiguous memory:
+//   Q4_K: unit(b, s, head, qs) for block b and 16-byte quant slice s;
+//   Q6_K: unit(b, h, l0, ql_a, ql_b, qh, sc4, dbits) (see q6k_load_unit).
 template <int QT, typename F>
-__device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, uint64_t nb,
-                                           uint8_t* lds, F&& f) {
+__device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, uint64_t nb, uint8_t* lds,
+                                            F&& unit) {
     if constexpr (QT == 12) {
+        // two units per iteration (g and g + stride), loads issued first
         const uint64_t units = nb * 8;
         const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-        for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < units; g += stride) {
-            const uint64_t b = g >> 3;
-            const int s = (int)(g & 7);
-            const uint8_t* bp = blocks + b * kQ4Bytes;
+        for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < units; g += 2 * stride) {
+            const uint64_t g2 = g + stride;
+            const bool two = g2 < units;
+            const uint8_t* bp = blocks + (g >> 3) * kQ4Bytes;
+            const uint8_t* bp2 = blocks + ((two ? g2 : g) >> 3) * kQ4Bytes;
             const uint4 head = *reinterpret_cast<const uint4*>(bp);
-            const uint4 qs = *reinterpret_cast<const uint4*>(bp + 16 + 16 * s);
-            Q4Unit u;
-            q4k_decode_unit(head, qs, s, u);
-            const uint64_t base = b * kQK + 64 * (s >> 1) + 16 * (s & 1);
-            f(base, u.lo);
-            f(base + 32, u.hi);
+            const uint4 qs = *reinterpret_cast<const uint4*>(bp + 16 + 16 * (int)(g & 7));
+            const uint4 head2 = *reinterpret_cast<const uint4*>(bp2);
+            const uint4 qs2 = *reinterpret_cast<const uint4*>(bp2 + 16 + 16 * (int)(g2 & 7));
+            unit(g >> 3, (int)(g & 7), head, qs);
+            if (two) unit(g2 >> 3, (int)(g2 & 7), head2, qs2);
         }
     } else {
         const uint64_t nchunks = (nb + kQ6Chunk - 1) / kQ6Chunk;
@@ -60,14 +63,34 @@ __device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, u
                 uint4 ql_a, ql_b, qh;
                 uint32_t sc4, dbits;
                 q6k_load_unit(lds, bl, h, l0, ql_a, ql_b, qh, sc4, dbits);
-                Q6Unit u;
-                q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
-                const uint64_t base = (b0 + bl) * kQK + 128 * h + l0;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) f(base + 32 * p, u.v[p]);
+                unit(b0 + bl, h, l0, ql_a, ql_b, qh, sc4, dbits);
             }
             __syncthreads();  // LDS is restaged by the next iteration
         }
+    }
+}
+
+// Calls f(first_element, vals[16]) for every run of 16 consecutive decoded
+// weights of the tensor.
+template <int QT, typename F>
+__device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, uint64_t nb, uint8_t* lds, F&& f) {
+    if constexpr (QT == 12) {
+        visit_units<12>(blocks, nb, lds, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+            Q4Unit u;
+            q4k_decode_unit(head, qs, s, u);
+            const uint64_t base = b * kQK + 64 * (s >> 1) + 16 * (s & 1);
+            f(base, u.lo);
+            f(base + 32, u.hi);
+        });
+    } else {
+        visit_units<14>(blocks, nb, lds,
+                        [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
+                            Q6Unit u;
+                            q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
+                            const uint64_t base = b * kQK + 128 * h + l0;
+#pragma unroll
+                            for (int p = 0; p < 4; ++p) f(base + 32 * p, u.v[p]);
+                        });
     }
 }
 
@@ -83,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void dequant_f32_kernel(const uint8_t* __
     });
 }
 
-// Pass 1: one absmax key per workgroup.
+// Pass 1: one absmax key per workgroup (from each unit's extreme quants).
 template <int QT>
 __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(const uint8_t* __restrict__ blocks,
                                                                uint64_t nb,
@@ -91,25 +114,33 @@ __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(const uint8_t* __
     __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
     __shared__ uint32_t red[kThreads / kWave];
     uint32_t key = 0;
-    visit_runs<QT>(blocks, nb, lds, [&](uint64_t, const float* v) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t k = abs_key(v[i]);
+    if constexpr (QT == 12) {
+        visit_units<12>(blocks, nb, lds, [&](uint64_t, int s, uint4 head, uint4 qs) {
+            const uint32_t k = q4k_unit_key(head, qs, s);
             key = key > k ? key : k;
-        }
-    });
+        });
+    } else {
+        visit_units<14>(blocks, nb, lds,
+                        [&](uint64_t, int, int, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
+                            const uint32_t k = q6k_unit_key(ql_a, ql_b, qh, sc4, dbits);
+                            key = key > k ? key : k;
+                        });
+    }
     key = block_max_u32<kThreads>(key, red);
     if (threadIdx.x == 0) partial[blockIdx.x] = key;
 }
 
-// Pass 2: reduce the pass-1 keys, derive the scales, encode.
+// Pass 2: reduce the pass-1 keys, derive the scales, encode.  Workgroup 0
+// publishes {a, q, dq, 0} to scale_out and, when given, to host_out
+// (host-visible memory the caller reads after synchronising the stream).
 template <int QT>
 __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __restrict__ blocks,
                                                                uint64_t nb,
                                                                const uint32_t* __restrict__ partial,
                                                                int npartial,
                                                                uint8_t* __restrict__ w_fp8,
-                                                               float* __restrict__ scale_out) {
+                                                               float* __restrict__ scale_out,
+                                                               float* __restrict__ host_out) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
     __shared__ uint32_t red[kThreads / kWave];
     const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
@@ -118,14 +149,49 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
         scale_out[1] = sc.q;
         scale_out[2] = sc.dq;
         scale_out[3] = 0.0f;
+        if (host_out) {
+            host_out[0] = sc.a;
+            host_out[1] = sc.q;
+            host_out[2] = sc.dq;
+            host_out[3] = 0.0f;
+        }
     }
     const float q = sc.q;
-    visit_runs<QT>(blocks, nb, lds, [&](uint64_t base, const float* v) {
-        uint32_t c[16];
+    // With a finite absmax and a unit whose f16 scales are finite, every
+    // product is finite and at most 448(1 + 2^-23) in magnitude: the wave
+    // takes the short encoder when all its lanes qualify.
+    const bool tensor_finite = sc.a <= 3.402823466e38f;
+    if constexpr (QT == 12) {
+        visit_units<12>(blocks, nb, lds, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+            Q4Unit u;
+            q4k_decode_unit(head, qs, s, u);
+            uint8_t* o = w_fp8 + b * kQK + 64 * (s >> 1) + 16 * (s & 1);
+            const bool fast = tensor_finite && half_finite(head.x) && half_finite(head.x >> 16);
+            if (__all(fast)) {
+                *reinterpret_cast<uint4*>(o) = e4m3_scaled16<true>(u.lo, q);
+                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16<true>(u.hi, q);
+            } else {
+                *reinterpret_cast<uint4*>(o) = e4m3_scaled16(u.lo, q);
+                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16(u.hi, q);
+            }
+        });
+    } else {
+        visit_units<14>(blocks, nb, lds,
+                        [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
+                            Q6Unit u;
+                            q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
+                            uint8_t* o = w_fp8 + b * kQK + 128 * h + l0;
+                            if (__all(tensor_finite && half_finite(dbits))) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = e4m3_scaled(v[i], q);
-        *reinterpret_cast<uint4*>(w_fp8 + base) = pack16(c);
-    });
+                                for (int p = 0; p < 4; ++p)
+                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16<true>(u.v[p], q);
+                            } else {
+#pragma unroll
+                                for (int p = 0; p < 4; ++p)
+                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16(u.v[p], q);
+                            }
+                        });
+    }
 }
 
 // Workgroups that cover the tensor once (one pass of the visit loop).
@@ -151,17 +217,17 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nb, flo
 }
 
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint8_t* w_fp8, uint8_t* ws,
-                       hipStream_t st) {
+                       float* host_scale, hipStream_t st) {
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
     const int g1 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
     const int g2 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
     if (qtype == 12) {
         pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out);
+        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale);
     } else {
         pack_absmax_kernel<14><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out);
+        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale);
     }
     return hipGetLastError();
 }

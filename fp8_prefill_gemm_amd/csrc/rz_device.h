@@ -23,47 +23,70 @@ constexpr float kFp8Max = 448.0f; // largest finite E4M3 value, code 0x7E
 //
 // FP32 -> E4M3 as the mod.rs page's conversion kernels define it: zero and
 // fp32 subnormals -> 0x00; Inf/NaN -> sign|0x7E; biased exponent E = e-120,
-// E < 1 flushes to 0x00 before any rounding, E > 15 saturates to sign|0x7E;
-// the 20 dropped fraction bits round to nearest even (round bit 19, sticky
-// bits 18..0) with a carry into E; a carry past E = 15 saturates.  A result
-// of E = 15, m = 7 (the NaN code in E4M3FN) is saturated to sign|0x7E too.
-// Pure integer arithmetic, so the result is bit-identical on any hardware.
-__device__ __forceinline__ uint32_t e4m3_from_bits(uint32_t u) {
-    const uint32_t s = (u >> 31) << 7;
-    const uint32_t e = (u >> 23) & 0xFFu;
-    const uint32_t f = u & 0x7FFFFFu;
-    int E = (int)e - 120;
-    uint32_t m3 = f >> 20;
-    const uint32_t rb = (f >> 19) & 1u;
-    const uint32_t sticky_or_odd = ((f & 0x7FFFFu) != 0u) | (m3 & 1u);
-    m3 += rb & sticky_or_odd;
-    E += (int)(m3 >> 3);
-    m3 &= 7u;
-    const bool sat = (e == 255u) | (E > 15) | ((E == 15) & (m3 == 7u));
-    const bool zero = ((int)e - 120) < 1;
-    uint32_t out = s | ((uint32_t)(E & 15) << 3) | m3;
-    out = sat ? (s | 0x7Eu) : out;
-    return zero ? 0u : out;
+// E < 1 (|y| < 2^-6) flushes to 0x00 before any rounding, E > 15 saturates to
+// sign|0x7E; the 20 dropped fraction bits round to nearest even with a carry
+// into E; a carry past E = 15, or a result of E = 15, m = 7 (the NaN code of
+// E4M3FN), saturates to sign|0x7E.  So every |y| >= 448 gives sign|0x7E.
+//
+// gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round-to-nearest-
+// even, which is the same map on 2^-6 <= |y| < 448.  Outside that range the
+// input is replaced first so that the converter returns the pages' code:
+// |y| < 2^-6 (and +-0, subnormals) -> +0 (0x00), |y| >= 448 and +-Inf ->
+// +-448 (sign|0x7E), NaN -> +448 (0x7E; the scaled conversions map a NaN
+// product to the code of the positive NaN).  The replacement plus the
+// converter agree with the bitwise definition above on all 2^32 fp32 bit
+// patterns except negative NaNs, which only the scaled path (0x7E) meets.
+__device__ __forceinline__ float e4m3_prep(float y) {
+    float t = __builtin_amdgcn_fmed3f(y, -kFp8Max, kFp8Max);
+    t = (fabsf(y) < 0.015625f) ? 0.0f : t;
+    return (y != y) ? kFp8Max : t;
+}
+
+// Fast form for values known to be finite with |y| <= 448 * (1 + 2^-23)
+// (a finite weight or activation times q = RN(448/a) with |x| <= a): only
+// the flush below 2^-6 remains; the converter rounds the rest to at most 448.
+__device__ __forceinline__ float e4m3_prep_finite(float y) { return (fabsf(y) < 0.015625f) ? 0.0f : y; }
+
+// Codes of four values in one word (byte i = value i).  The converter writes
+// src0 to the low byte of the selected 16-bit half and src1 to the high one.
+template <bool kFinite = false>
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    if constexpr (kFinite) {
+        a = e4m3_prep_finite(a);
+        b = e4m3_prep_finite(b);
+        c = e4m3_prep_finite(c);
+        d = e4m3_prep_finite(d);
+    } else {
+        a = e4m3_prep(a);
+        b = e4m3_prep(b);
+        c = e4m3_prep(c);
+        d = e4m3_prep(d);
+    }
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
 // E4M3 code of RN(x * q).  The product is one IEEE multiply (no contraction:
 // there is nothing to fuse it with, and the build uses -ffp-contract=off).
-// A NaN product encodes as the positive NaN does, 0x7E.
 __device__ __forceinline__ uint32_t e4m3_scaled(float x, float q) {
-    const float y = x * q;
-    const uint32_t code = e4m3_from_bits(__float_as_uint(y));
-    return (y != y) ? 0x7Eu : code;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(x * q), 0.0f, 0, false) & 0xFFu;
 }
 
-// Pack 16 codes (one per float) into a uint4, byte i of the result = code i.
-__device__ __forceinline__ uint4 pack16(const uint32_t c[16]) {
+// Codes of RN(v[i] * q), i < 16, byte i of the result = code i.  kFinite:
+// every product is known to be finite with |y| <= 448 * (1 + 2^-23).
+template <bool kFinite = false>
+__device__ __forceinline__ uint4 e4m3_scaled16(const float v[16], float q) {
     uint4 r;
-    r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    r.z = c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24);
-    r.w = c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24);
+    r.x = e4m3_pack4<kFinite>(v[0] * q, v[1] * q, v[2] * q, v[3] * q);
+    r.y = e4m3_pack4<kFinite>(v[4] * q, v[5] * q, v[6] * q, v[7] * q);
+    r.z = e4m3_pack4<kFinite>(v[8] * q, v[9] * q, v[10] * q, v[11] * q);
+    r.w = e4m3_pack4<kFinite>(v[12] * q, v[13] * q, v[14] * q, v[15] * q);
     return r;
 }
+
+// f16 bit pattern (low 16 bits) of a finite value.
+__device__ __forceinline__ bool half_finite(uint32_t h) { return (h & 0x7C00u) != 0x7C00u; }
 
 // ---------------------------------------------------------------- absmax
 //
@@ -177,12 +200,53 @@ __device__ __forceinline__ void q4k_decode_unit(uint4 head, uint4 qs, int s, Q4U
     q4k_scale_min(head, 2 * c + 1, sc1, m1);
     const float d0 = d * (float)sc0, o0 = dmin * (float)m0;
     const float d1 = d * (float)sc1, o1 = dmin * (float)m1;
+    const uint32_t w[4] = {qs.x, qs.y, qs.z, qs.w};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const uint32_t b = byte_of(qs, t);
-        u.lo[t] = d0 * (float)(b & 15u) - o0;
-        u.hi[t] = d1 * (float)(b >> 4) - o1;
+    for (int i = 0; i < 4; ++i) {
+        // quant bytes 4i..4i+3: low nibbles -> lo, high nibbles -> hi (one
+        // byte-to-float conversion per value)
+        uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+        asm("" : "+v"(lo), "+v"(hi));  // keep the masks: byte b converts with v_cvt_f32_ubyte<b>
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            u.lo[4 * i + b] = d0 * (float)((lo >> (8 * b)) & 0xFFu) - o0;
+            u.hi[4 * i + b] = d1 * (float)((hi >> (8 * b)) & 0xFFu) - o1;
+        }
     }
+}
+
+// max abs_key over the 32 decoded values of a unit, without decoding them:
+// d*sc*q is exact, so q -> RN(d*sc*q - dmin*m) is monotone in q and |value|
+// peaks at the smallest or the largest nibble of each half (NaN products
+// only occur where every value of the half is NaN or at q = 0 next to Inf
+// values, so the endpoint keys still give the maximum).
+__device__ __forceinline__ uint32_t q4k_unit_key(uint4 head, uint4 qs, int s) {
+    const float d = half_bits_to_float(head.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(head.x >> 16);
+    const int c = s >> 1;
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(head, 2 * c, sc0, m0);
+    q4k_scale_min(head, 2 * c + 1, sc1, m1);
+    const float d0 = d * (float)sc0, o0 = dmin * (float)m0;
+    const float d1 = d * (float)sc1, o1 = dmin * (float)m1;
+    const uint32_t w[4] = {qs.x, qs.y, qs.z, qs.w};
+    float lmax = 0.0f, lmin = 15.0f, hmax = 0.0f, hmin = 15.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float ql = (float)((lo >> (8 * b)) & 0xFFu), qh = (float)((hi >> (8 * b)) & 0xFFu);
+            lmax = fmaxf(lmax, ql);
+            lmin = fminf(lmin, ql);
+            hmax = fmaxf(hmax, qh);
+            hmin = fminf(hmin, qh);
+        }
+    }
+    const uint32_t k0 = abs_key(d0 * lmax - o0), k1 = abs_key(d0 * lmin - o0);
+    const uint32_t k2 = abs_key(d1 * hmax - o1), k3 = abs_key(d1 * hmin - o1);
+    const uint32_t a = k0 > k1 ? k0 : k1, b = k2 > k3 ? k2 : k3;
+    return a > b ? a : b;
 }
 
 // Q6_K: one unit is (half h, l0 in {0,16}) of a super-block: 64 weights, four
@@ -200,18 +264,59 @@ __device__ __forceinline__ void q6k_decode_unit(uint4 ql_a, uint4 ql_b, uint4 qh
     float ds[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) ds[p] = d * (float)(int8_t)((sc4 >> (8 * p)) & 0xFFu);
+    const uint32_t A[4] = {ql_a.x, ql_a.y, ql_a.z, ql_a.w};
+    const uint32_t B[4] = {ql_b.x, ql_b.y, ql_b.z, ql_b.w};
+    const uint32_t H[4] = {qh.x, qh.y, qh.z, qh.w};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const uint32_t a = byte_of(ql_a, t), b = byte_of(ql_b, t), h = byte_of(qh, t);
-        const int q0 = (int)((a & 15u) | ((h & 3u) << 4)) - 32;
-        const int q1 = (int)((b & 15u) | (((h >> 2) & 3u) << 4)) - 32;
-        const int q2 = (int)((a >> 4) | (((h >> 4) & 3u) << 4)) - 32;
-        const int q3 = (int)((b >> 4) | (((h >> 6) & 3u) << 4)) - 32;
-        u.v[0][t] = ds[0] * (float)q0;
-        u.v[1][t] = ds[1] * (float)q1;
-        u.v[2][t] = ds[2] * (float)q2;
-        u.v[3][t] = ds[3] * (float)q3;
+    for (int i = 0; i < 4; ++i) {
+        // the 6-bit quants of bytes 4i..4i+3, one per byte lane
+        uint32_t q[4];
+        q[0] = (A[i] & 0x0F0F0F0Fu) | ((H[i] & 0x03030303u) << 4);
+        q[1] = (B[i] & 0x0F0F0F0Fu) | (((H[i] >> 2) & 0x03030303u) << 4);
+        q[2] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 4) & 0x03030303u) << 4);
+        q[3] = ((B[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 6) & 0x03030303u) << 4);
+        asm("" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]));
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) u.v[p][4 * i + b] = ds[p] * ((float)((q[p] >> (8 * b)) & 0xFFu) - 32.0f);
     }
+}
+
+// max abs_key over the 64 decoded values of a unit, from the smallest and
+// largest 6-bit quant of each run of 16 (d*sc*(q-32) is exact and monotone
+// in q).
+__device__ __forceinline__ uint32_t q6k_unit_key(uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
+    const float d = half_bits_to_float(dbits);
+    const uint32_t A[4] = {ql_a.x, ql_a.y, ql_a.z, ql_a.w};
+    const uint32_t B[4] = {ql_b.x, ql_b.y, ql_b.z, ql_b.w};
+    const uint32_t H[4] = {qh.x, qh.y, qh.z, qh.w};
+    float qmax[4] = {0.0f, 0.0f, 0.0f, 0.0f}, qmin[4] = {63.0f, 63.0f, 63.0f, 63.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t q[4];
+        q[0] = (A[i] & 0x0F0F0F0Fu) | ((H[i] & 0x03030303u) << 4);
+        q[1] = (B[i] & 0x0F0F0F0Fu) | (((H[i] >> 2) & 0x03030303u) << 4);
+        q[2] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 4) & 0x03030303u) << 4);
+        q[3] = ((B[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 6) & 0x03030303u) << 4);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float f = (float)((q[p] >> (8 * b)) & 0xFFu);
+                qmax[p] = fmaxf(qmax[p], f);
+                qmin[p] = fminf(qmin[p], f);
+            }
+    }
+    uint32_t key = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float ds = d * (float)(int8_t)((sc4 >> (8 * p)) & 0xFFu);
+        const uint32_t k0 = abs_key(ds * (qmax[p] - 32.0f)), k1 = abs_key(ds * (qmin[p] - 32.0f));
+        key = key > k0 ? key : k0;
+        key = key > k1 ? key : k1;
+    }
+    return key;
 }
 
 // Stage `nb` (<= 64) consecutive Q6_K blocks starting at `src` (16-byte

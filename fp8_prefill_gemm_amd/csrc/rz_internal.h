@@ -18,9 +18,10 @@ constexpr size_t kWsBytes = 8448;
 hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nblocks, float* out,
                               hipStream_t st);
 // Two kernels: partial absmax keys, then (reduce + encode).  Writes
-// {a, q, dq} as floats at ws + kWsScaleOffset.
+// {a, q, dq, 0} as floats at ws + kWsScaleOffset and, when host_scale is not
+// null, to that device-accessible host memory too.
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nblocks, uint8_t* w_fp8,
-                       uint8_t* ws, hipStream_t st);
+                       uint8_t* ws, float* host_scale, hipStream_t st);
 
 // ---- actquant.hip
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,
