@@ -231,8 +231,10 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][4], const uint8_t* cur, uin
 // tiles.  G = one workgroup per CU; the first R*G tiles (R = floor(T/G) full
 // rounds, chosen as whole n-columns of tiles) run one tile per workgroup.
 // The rem = T - R*G tiles left over would leave most CUs idle for a whole
-// tile time, so each of them is split along K into s chunks (s*rem <= G)
-// that run in parallel, as workgroups after the whole tiles in the same
+// tile time, so each of them is split along K into s chunks (s*rem <= G;
+// s <= 2: each extra chunk adds a 256 KB partial sum to write and read back,
+// which costs more than the finer balance gains) that run in parallel, as
+// workgroups after the whole tiles in the same
 // launch; the chunks store partial sums in a workspace, and the last chunk
 // of a tile to finish adds the s partial sums in chunk order (so the result
 // does not depend on the arrival order) and writes the output.  No
@@ -704,7 +706,7 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
         const int per_xcd = ceil_div(p.rem, kXcds);
         if (p.rem > 0 && p.rem <= cus && split_allowed) {
             int s = (cus / kXcds) / per_xcd;
-            s = s < 1 ? 1 : (s > 4 ? 4 : s);
+            s = s < 1 ? 1 : (s > 2 ? 2 : s);
             p.s = s > pairs / 2 ? pairs / 2 : s;  // chunks of >= 2 pairs (>= 4 K-steps)
         }
         if (p.s > 1) {

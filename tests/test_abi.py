@@ -157,21 +157,21 @@ def test_plans_cover_shapes(L):
 def _interior_wgs(tiles_m, tiles_n, k, cus=256):
     """Workgroups of an interior-tile plan (256 CUs without a device): whole
     tiles for the full rounds, then the leftover tiles split along K into s
-    chunks per tile (s*leftover <= CUs, chunks of >= 2 K pairs), or every
-    tile whole when no split fits."""
+    chunks per tile (s <= 2, s*leftover <= CUs, chunks of >= 2 K pairs), or
+    every tile whole when no split fits."""
     t = tiles_m * tiles_n
     r = t // cus
     if (r * cus) % tiles_m:
         r = 0
     rem = t - r * cus
     per_xcd = -(-rem // 8)
-    s = min(4, max(1, (cus // 8) // per_xcd), (k // 256) // 2) if 0 < rem <= cus else 1
+    s = min(2, max(1, (cus // 8) // per_xcd), (k // 256) // 2) if 0 < rem <= cus else 1
     return r * cus + 8 * per_xcd * s if s > 1 else t
 
 
 def test_interior_plan_examples(L):
-    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles in 3 K chunks
-    assert rz.rz_fp8_gemm_plan(2048, 18944, 3584)[3] == 512 + 240
+    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles in 2 K chunks
+    assert rz.rz_fp8_gemm_plan(2048, 18944, 3584)[3] == 512 + 160
     # FFN down at M=2048: 112 tiles, all split in 2 K chunks
     assert rz.rz_fp8_gemm_plan(2048, 3584, 18944)[3] == 224
     # M=4096: 1184 tiles, 160 left over is too many to split: all whole

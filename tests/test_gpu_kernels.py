@@ -265,12 +265,13 @@ def _codes(g, shape):
 
 
 @pytest.mark.parametrize("m,n,k,full", [
-    (2048, 2560, 1536, True),    # 80 tiles: all split in 3 K chunks of 2 pairs
-    (2048, 2560, 2816, False),   # 80 tiles in 3 uneven chunks (3, 4, 4 pairs)
+    (2048, 2560, 1536, True),    # 80 tiles: all split in 2 K chunks of 3 pairs
+    (2048, 2560, 2816, False),   # 80 tiles in 2 uneven chunks (5, 6 pairs)
     (2048, 2560, 768, True),     # 80 tiles, K too short to split: whole tiles
-    (2048, 3584, 1024, True),    # 112 tiles: all split in 2
+    (2048, 3584, 1024, True),    # 112 tiles: all split in 2 chunks of 2 pairs
     (2048, 10240, 1024, False),  # 320 tiles: one whole round + 64 tiles split in 2
     (4096, 4096, 512, False),    # 256 tiles: exactly one round
+    (4096, 4608, 1024, False),   # 288 tiles: one round + 32 split tiles
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
     bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
