@@ -144,7 +144,10 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* st
     }
 }
 
-// Per-lane LDS offsets of the persistent kernel, computed once.  The swizzle
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+// Per-lane LDS offsets of the K loop, computed once.  The swizzle
 // only depends on row bits 0..4, so every row the lane touches (its own row
 // plus multiples of 32) shares it and all addresses differ by immediates.
 struct PipeOffsets {
@@ -153,6 +156,7 @@ struct PipeOffsets {
     uint32_t fb[2][2];   // activation fragment (includes the 256*128 operand base)
 };
 
+template <int TM>
 __device__ __forceinline__ PipeOffsets pipe_offsets(int tid, int wn, int wm, int lane) {
     PipeOffsets o;
     const int r = tid >> 3;
@@ -164,7 +168,7 @@ __device__ __forceinline__ PipeOffsets pipe_offsets(int tid, int wn, int wm, int
         for (int h = 0; h < 2; ++h) {
             const int chunk = ((kk * 4 + (lane >> 5) * 2 + h) ^ sl) << 4;
             o.fa[kk][h] = (uint32_t)((wn * 128 + lr) * kBK + chunk);
-            o.fb[kk][h] = (uint32_t)(256 * kBK + (wm * 128 + lr) * kBK + chunk);
+            o.fb[kk][h] = (uint32_t)(256 * kBK + (wm * 32 * TM + lr) * kBK + chunk);
         }
     return o;
 }
@@ -175,50 +179,94 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* base, uint32_t lo, uint32_
     return __builtin_bit_cast(v8i, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One 128-byte K-step of the persistent kernel for one wave (256x256 tile,
-// 2x2 waves of 128x128: 4x4 MFMA tiles of 32x32, two 64-byte K halves).
-//   cur  LDS slot holding this step's operands (weight rows, then activation
-//        rows, 128 bytes each);
+// One 128-byte K-step for one wave of a 256 x (64*TM) tile: 2x2 waves of
+// 128 x 32*TM, i.e. 4 x TM MFMA tiles of 32x32, two 64-byte K halves
+// (TM = 4: whole 256x256 tile; TM = 2: half tile of 128 activation rows).
+//   cur  LDS slot holding this step's operands (256 weight rows, then the
+//        activation rows, 128 bytes each);
 //   nxt  the other slot, which receives the next step's operands;
-//   x    16 staged 16-byte chunks per thread holding the next step's data
-//        (chunks 0..7 weight rows tid/8 + 32c, 8..15 activation rows); each
-//        is written to `nxt` and then refilled from global memory with the
-//        K-step three ahead of this one (byte offset kb; rsrc wrs / ars).
-// The step is eight MFMA groups (one activation fragment against the four
+//   x    8 + 2*TM staged 16-byte chunks per thread holding the next step's
+//        data (chunks 0..7 weight rows tid/8 + 32c, then activation rows);
+//        each is written to `nxt` and then refilled from global memory with
+//        the K-step three ahead of this one (byte offset kb; rsrc wrs / ars).
+// The step is 2*TM MFMA groups (one activation fragment against the four
 // weight fragments of one K half).  A sched_barrier closes every group, so
-// the program order is exactly: fragment reads for the next group, 4 MFMAs,
-// 2 chunk writes, 2 chunk loads.  A chunk load therefore has two full steps
-// to land before the same group of the step after next writes it to LDS.
-// The caller places a workgroup barrier after each step.
-__device__ __forceinline__ void kstep(v16f (&acc)[4][4], const uint8_t* cur, uint8_t* nxt, u32x4 (&x)[16],
-                                      __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars, uint32_t voff,
-                                      uint32_t kb, uint32_t step, const PipeOffsets& o) {
+// the program order is exactly: fragment reads for the next group, 4 MFMAs
+// with the group's chunk writes and loads between them (2 of each for
+// TM = 4, 3 for TM = 2).  A chunk load therefore has two full steps to land
+// before the same group of the step after next writes it to LDS.  The
+// caller places a workgroup barrier after each step.
+template <int TM>
+__device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, uint8_t* nxt,
+                                      u32x4 (&x)[8 + 2 * TM], __amdgpu_buffer_rsrc_t wrs,
+                                      __amdgpu_buffer_rsrc_t ars, uint32_t voff, uint32_t kb, uint32_t step,
+                                      const PipeOffsets& o) {
+    static_assert(TM == 4 || TM == 2, "whole or half tile");
     constexpr int kRow32 = 32 * kBK;  // 32 rows
+    constexpr int kGroups = 2 * TM;
+    constexpr int kPer = (8 + 2 * TM) / kGroups;  // chunks per group
+    constexpr int kA1 = TM == 4 ? 1 : 0;          // groups kA1, kA1+1 read the second K half's weights
     v8i a[2][4];
     v8i b[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[0][i] = frag_at(cur + i * kRow32, o.fa[0][0], o.fa[0][1]);
+    // b first: LDS reads complete in order, so MFMA i of group 0 waits only
+    // for b[0] and a[0][0..i]
     b[0] = frag_at(cur, o.fb[0][0], o.fb[0][1]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        const int kk = g >> 2, j = g & 3;
-        if (g < 7) {
-            const int gn = g + 1;
-            b[gn & 1] = frag_at(cur + (gn & 3) * kRow32, o.fb[gn >> 2][0], o.fb[gn >> 2][1]);
-        }
-        if (g == 1 || g == 2) {  // second K half's weight fragments, two per group
+    for (int i = 0; i < 4; ++i) a[0][i] = frag_at(cur + i * kRow32, o.fa[0][0], o.fa[0][1]);
 #pragma unroll
-            for (int i = 2 * (g - 1); i < 2 * g; ++i) a[1][i] = frag_at(cur + i * kRow32, o.fa[1][0], o.fa[1][1]);
+    for (int g = 0; g < kGroups; ++g) {
+        const int kk = g / TM, j = g % TM;
+        if (g < kGroups - 1) {
+            const int gn = g + 1;
+            b[gn & 1] = frag_at(cur + (gn % TM) * kRow32, o.fb[gn / TM][0], o.fb[gn / TM][1]);
+        }
+        if (g == kA1 || g == kA1 + 1) {  // two weight fragments per group
+#pragma unroll
+            for (int i = 2 * (g - kA1); i < 2 * (g - kA1) + 2; ++i)
+                a[1][i] = frag_at(cur + i * kRow32, o.fa[1][0], o.fa[1][1]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[g & 1], acc[i][j], 0, 0, 0,
                                                                         0, 0, 0);
 #pragma unroll
-        for (int c = 2 * g; c < 2 * g + 2; ++c) {
+        for (int c = kPer * g; c < kPer * g + kPer; ++c) {
             *reinterpret_cast<u32x4*>(nxt + (c >> 3) * 256 * kBK + (c & 7) * kRow32 + o.st) = x[c];
             x[c] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, kb + (c & 7) * step, 0));
+        }
+        // order inside the group: the fragment reads (group 0 also holds the
+        // 10 reads before the loop), then each chunk write and each load in
+        // the shadow of an MFMA
+        if constexpr (TM == 4) {
+            if (g == 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+            else if (g == 1 || g == 2)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+            else if (g < 7)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        } else {
+            if (g == 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 16, 0);
+            else if (g == 1)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+            else if (g == 2)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -231,98 +279,95 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][4], const uint8_t* cur, uin
 // tiles.  G = one workgroup per CU; the first R*G tiles (R = floor(T/G) full
 // rounds, chosen as whole n-columns of tiles) run one tile per workgroup.
 // The rem = T - R*G tiles left over would leave most CUs idle for a whole
-// tile time, so each of them is split along K into s chunks (s*rem <= G;
-// s <= 2: each extra chunk adds a 256 KB partial sum to write and read back,
-// which costs more than the finer balance gains) that run in parallel, as
-// workgroups after the whole tiles in the same
-// launch; the chunks store partial sums in a workspace, and the last chunk
-// of a tile to finish adds the s partial sums in chunk order (so the result
-// does not depend on the arrival order) and writes the output.  No
-// workgroup waits for another.
+// tile time; when 2*rem <= G each of them is cut into two half tiles of 128
+// activation rows that run on two CUs, as workgroups after the whole tiles
+// in the same launch, so the last round takes about half a tile time.  A
+// half tile runs the whole K range and stores its own output: no partial
+// sums, no workspace, no workgroup waits for another.
 //
 // The K loop (tile_mainloop): two LDS slots, the global loads three K-steps
 // ahead of the MFMAs in two register sets.
 // ---------------------------------------------------------------------------
 
-// Origin of tile t in the grouped order of a tiles_m x tiles_n region
-// (groups of gm m-tiles, m fastest inside a group).
-__device__ __forceinline__ void grouped_origin(int t, int tiles_m, int tiles_n, int gm_full, int& n0,
-                                               int& m0) {
+// Origin of tile t of BN x BM tiles in the grouped order of a tiles_m x
+// tiles_n region (groups of gm m-tiles, m fastest inside a group).
+template <int BN, int BM>
+__device__ __forceinline__ void grouped_origin_bb(int t, int tiles_m, int tiles_n, int gm_full, int& n0, int& m0) {
     const int per_group = gm_full * tiles_n;
     const int gidx = t / per_group;
     const int first_m = gidx * gm_full;
     const int gm = (tiles_m - first_m) < gm_full ? (tiles_m - first_m) : gm_full;
     const int tin = t - gidx * per_group;
-    n0 = (tin / gm) * 256;
-    m0 = (first_m + tin % gm) * 256;
+    n0 = (tin / gm) * BN;
+    m0 = (first_m + tin % gm) * BM;
 }
 
-// acc (or acc*scale) over the K-steps [k0, k0+KS) of the tile whose weight
-// rows start at `wrs` and activation rows at `ars` (KS even, >= 4).
+// acc over the K-steps [0, KS) of the 256 x 64*TM tile whose weight rows
+// start at `wrs` and activation rows at `ars` (KS even, >= 4).
 //
 // K-step t computes from LDS slot t%2 while register set (t%2 ? xq : xp)
 // moves the data of step t+1 into the other slot and is refilled with step
 // t+3; so each load has two steps of MFMA work to land.
-__device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][4], uint8_t (&smem)[2][512 * kBK],
+template <int TM>
+__device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][TM], uint8_t (&smem)[2][512 * kBK],
                                               __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars,
-                                              uint32_t voff, uint32_t step, int k0, int KS,
-                                              const PipeOffsets& po) {
+                                              uint32_t voff, uint32_t step, int KS, const PipeOffsets& po) {
+    constexpr int kC = 8 + 2 * TM;  // staged chunks per thread
     const __amdgpu_buffer_rsrc_t zr = tile_rsrc(nullptr, 0u);  // range 0: loads return 0, no traffic
-    const uint32_t kb0 = (uint32_t)k0 * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
-    u32x4 xp[16], xq[16];
+        for (int j = 0; j < TM; ++j) acc[i][j] = (v16f){};
+    u32x4 xp[kC], xq[kC];
     // K-step 0 -> slot 0 (through xq), K-step 1 -> xp, K-step 2 -> xq
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        xq[c] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, kb0 + (c & 7) * step, 0));
+    for (int c = 0; c < kC; ++c)
+        xq[c] = __builtin_bit_cast(u32x4,
+                                   __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, (c & 7) * step, 0));
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        xp[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff,
-                                                                                kb0 + kBK + (c & 7) * step, 0));
+    for (int c = 0; c < kC; ++c)
+        xp[c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, kBK + (c & 7) * step, 0));
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
+    for (int c = 0; c < kC; ++c)
         *reinterpret_cast<u32x4*>(smem[0] + (c >> 3) * 256 * kBK + (c & 7) * 32 * kBK + po.st) = xq[c];
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        xq[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              c < 8 ? wrs : ars, voff, kb0 + 2 * kBK + (c & 7) * step, 0));
+    for (int c = 0; c < kC; ++c)
+        xq[c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? wrs : ars, voff, 2 * kBK + (c & 7) * step, 0));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < KS; kt += 2) {
         const bool in3 = kt + 3 < KS, in4 = kt + 4 < KS;
-        kstep(acc, smem[0], smem[1], xp, in3 ? wrs : zr, in3 ? ars : zr, voff, kb0 + (uint32_t)(kt + 3) * kBK, step,
-              po);
+        kstep<TM>(acc, smem[0], smem[1], xp, in3 ? wrs : zr, in3 ? ars : zr, voff, (uint32_t)(kt + 3) * kBK, step,
+                  po);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        kstep(acc, smem[1], smem[0], xq, in4 ? wrs : zr, in4 ? ars : zr, voff, kb0 + (uint32_t)(kt + 4) * kBK, step,
-              po);
+        kstep<TM>(acc, smem[1], smem[0], xq, in4 ? wrs : zr, in4 ? ars : zr, voff, (uint32_t)(kt + 4) * kBK, step,
+                  po);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// acc * mul -> a 256x256 fp32 tile at byte offset 4*(row*stride + nb + col)
-// of `rs` (float4 runs of the output column).  For the output, `rs` covers
-// the tile's valid rows only, so the stores of rows m >= M fall outside the
-// buffer range and are dropped by the hardware (no branches).
-__device__ __forceinline__ void store_acc(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t rs, uint32_t stride,
-                                          uint32_t nb, int wn, int wm, int lane, float mul) {
+// acc * scale -> the 256 x 64*TM output tile at (n0, m0), float4 runs of an
+// output row.  `rs` covers the valid rows from m0 only, so the stores of
+// rows m >= M fall outside the buffer range and are dropped by the hardware
+// (no branches).
+template <int TM>
+__device__ __forceinline__ void store_acc(const v16f (&acc)[4][TM], __amdgpu_buffer_rsrc_t rs, uint32_t N,
+                                          uint32_t n0, int wn, int wm, int lane, float scale) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t row = (uint32_t)(wm * 128 + j * 32 + (lane & 31));
+        for (int j = 0; j < TM; ++j) {
+            const uint32_t row = (uint32_t)(wm * 32 * TM + j * 32 + (lane & 31));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t col = nb + (uint32_t)(wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
-                const float4 v = make_float4(acc[i][j][4 * q] * mul, acc[i][j][4 * q + 1] * mul,
-                                             acc[i][j][4 * q + 2] * mul, acc[i][j][4 * q + 3] * mul);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (row * stride + col) * 4u, 0,
-                                                       0);
+                const uint32_t col = n0 + (uint32_t)(wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
+                const float4 v = make_float4(acc[i][j][4 * q] * scale, acc[i][j][4 * q + 1] * scale,
+                                             acc[i][j][4 * q + 2] * scale, acc[i][j][4 * q + 3] * scale);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (row * N + col) * 4u, 0, 0);
             }
         }
     }
@@ -335,127 +380,161 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
 }
 
 // Work of the interior-tile kernel.  The grid is nwhole whole-tile
-// workgroups followed by the K chunks of the split tiles.
+// workgroups followed by the half tiles.
 //   Whole tiles: the first nd n-columns of tiles (all m), in the grouped
 //   order (groups of group_m m-tiles).  The dispatcher sends workgroup w to
 //   XCD w % 8, so XCD x is given the contiguous range [x*T/8, (x+1)*T/8) of
 //   that order: the workgroups that run together on one XCD share weight
 //   and activation rows through its L2.
-//   Split tiles: n-columns [nd, tiles_n), rem tiles in a grouped order with
-//   groups of tail_gm m-tiles.  XCD x owns the tiles [x*per_xcd,
-//   (x+1)*per_xcd) and its workgroups take them chunk by chunk, so the s
-//   chunks of a tile run on one XCD, whose L2 is coherent for its CUs.
-//   Chunk c covers the 256-byte K pairs [c*pairs/s, (c+1)*pairs/s).
+//   Half tiles: n-columns [nd, tiles_n) by 2*tiles_m activation halves of
+//   128 rows, nhalf of them in a grouped order with groups of half_gm
+//   halves; XCD x again takes a contiguous range of that order.
 struct InteriorPlan {
     int tiles_m, nd, nwhole, group_m;
-    int rem, tail_gm, per_xcd, s, pairs;
+    int nhalf, half_gm;
 };
 
-// Split-tile epilogue, after the chunk has stored its partial sum (a
-// 256x256 fp32 tile, row stride 256) in its slot: wait until the stores
-// have reached the XCD's L2 and count in.  The last chunk to arrive resets
-// the counter, adds the s partial sums in chunk order, scales, and writes
-// the output: float4 f of the tile (row f/64, columns 4*(f%64)..+3), 64
-// per thread, NB at a time (NB*S loads in flight per thread).
-template <int S, int NB>
-__device__ __forceinline__ void split_finish(const float* __restrict__ parts, unsigned* arr, unsigned& arrival,
-                                             __amdgpu_buffer_rsrc_t yrs, int N, int n0, int tid, float scale) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) arrival = __hip_atomic_fetch_add(arr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != (unsigned)(S - 1)) return;
-    if (tid == 0) __hip_atomic_store(arr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
-    const __amdgpu_buffer_rsrc_t prs =
-        tile_rsrc(reinterpret_cast<const uint8_t*>(parts), (uint32_t)S * 256u * 256u * 4u);
-    for (int f0 = 0; f0 < 64; f0 += NB) {
-        u32x4 v[S][NB];
-#pragma unroll
-        for (int c = 0; c < S; ++c)
-#pragma unroll
-            for (int u = 0; u < NB; ++u)  // sc0: not from this CU's L1
-                v[c][u] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               prs, ((uint32_t)c * 65536u + (uint32_t)((f0 + u) * 256 + tid) * 4u) * 4u, 0, 1));
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const uint32_t f = (uint32_t)((f0 + u) * 256 + tid);
-            float r[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float sum = __uint_as_float(v[0][u][e]);
-#pragma unroll
-                for (int c = 1; c < S; ++c) sum += __uint_as_float(v[c][u][e]);
-                r[e] = sum * scale;
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, make_float4(r[0], r[1], r[2], r[3])), yrs,
-                                                   ((f >> 6) * (uint32_t)N + (uint32_t)n0 + 4u * (f & 63u)) * 4u, 0, 0);
-        }
-    }
+// Contiguous share of XCD x (workgroup w) of T items in order; false if w
+// has none.
+__device__ __forceinline__ bool xcd_item(int w, int T, int& t) {
+    const int tall = T / kXcds, rem = T % kXcds;
+    const int x = w % kXcds, loc = w / kXcds;
+    if (loc >= tall + (x < rem ? 1 : 0)) return false;
+    t = x * tall + (x < rem ? x : rem) + loc;
+    return true;
 }
 
-__global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M, int N, int K,
-    const float* __restrict__ act_scale, float w_scale, InteriorPlan P, float* __restrict__ part,
-    unsigned* __restrict__ cnt) {
+__global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* __restrict__ A,
+                                                                const uint8_t* __restrict__ Wt, float* __restrict__ Y,
+                                                                int M, int N, int K,
+                                                                const float* __restrict__ act_scale, float w_scale,
+                                                                InteriorPlan P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
-    __shared__ unsigned arrival;
 
     const int bid = blockIdx.x;
-    int n0, m0, k0 = 0, KS = K / kBK, tl = -1, chunk = 0;
-    if (bid < P.nwhole) {
-        const int T = P.nwhole;
-        const int tall = T / kXcds, rem = T % kXcds;
-        const int x = bid % kXcds, loc = bid / kXcds;
-        grouped_origin(x * tall + (x < rem ? x : rem) + loc, P.tiles_m, P.nd, P.group_m, n0, m0);
-    } else {
-        const int g = bid - P.nwhole;  // nwhole is a multiple of 8: same XCD
-        const int x = g % kXcds, j = g / kXcds;
-        const int base = x * P.per_xcd;
-        int count = P.rem - base;
-        count = count < P.per_xcd ? count : P.per_xcd;
-        if (count <= 0 || j >= count * P.s) return;
-        tl = base + j / P.s;
-        chunk = j % P.s;
-        grouped_origin(tl, P.tiles_m, (N >> 8) - P.nd, P.tail_gm, n0, m0);
-        n0 += P.nd * 256;
-        const int p0 = chunk * P.pairs / P.s, p1 = (chunk + 1) * P.pairs / P.s;
-        k0 = 2 * p0;
-        KS = 2 * (p1 - p0);
-    }
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int wn = wid & 1, wm = wid >> 1;
     const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
-    const PipeOffsets po = pipe_offsets(tid, wn, wm, lane);
-
-    v16f acc[4][4];
-    tile_mainloop(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
-                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, 32u * (uint32_t)K, k0, KS, po);
-    const __amdgpu_buffer_rsrc_t yrs = tile_out_rsrc(Y, M, N, m0);
+    const uint32_t step = 32u * (uint32_t)K;
     const float scale = act_scale[1] * w_scale;
-    // One store for both kinds of work: a whole tile writes acc*scale to Y;
-    // a K chunk writes acc (times 1, exact) to its partial slot.
-    float* parts = tl < 0 ? nullptr : part + (size_t)tl * P.s * (256 * 256);
-    const __amdgpu_buffer_rsrc_t srs =
-        tl < 0 ? yrs : tile_rsrc(reinterpret_cast<const uint8_t*>(parts + (size_t)chunk * (256 * 256)), 256u * 256u * 4u);
-    store_acc(acc, srs, tl < 0 ? (uint32_t)N : 256u, tl < 0 ? (uint32_t)n0 : 0u, wn, wm, lane, tl < 0 ? scale : 1.0f);
-    if (tl < 0) return;
-    unsigned* arr = cnt + tl;  // arrival counters [0, rem); partial slots follow
-    switch (P.s) {
-        case 2: split_finish<2, 16>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
-        case 3: split_finish<3, 16>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
-        default: split_finish<4, 8>(parts, arr, arrival, yrs, N, n0, tid, scale); break;
+    int t, n0, m0;
+    if (bid < P.nwhole) {
+        (void)xcd_item(bid, P.nwhole, t);
+        grouped_origin_bb<256, 256>(t, P.tiles_m, P.nd, P.group_m, n0, m0);
+        const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
+        v16f acc[4][4];
+        tile_mainloop<4>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+                         tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
+        store_acc<4>(acc, tile_out_rsrc(Y, M, N, m0), (uint32_t)N, (uint32_t)n0, wn, wm, lane, scale);
+        return;
     }
+    // nwhole is a multiple of 8: the half tiles' workgroups keep w % 8
+    if (!xcd_item(bid - P.nwhole, P.nhalf, t)) return;
+    grouped_origin_bb<256, 128>(t, 2 * P.tiles_m, (N >> 8) - P.nd, P.half_gm, n0, m0);
+    n0 += P.nd * 256;
+    const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
+    v16f acc[4][2];
+    tile_mainloop<2>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+                     tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
+    store_acc<2>(acc, tile_out_rsrc(Y, M, N, m0), (uint32_t)N, (uint32_t)n0, wn, wm, lane, scale);
 }
 
-template <int BN, int BM, int WN, int WM>
+// ---------------------------------------------------------------------------
+// Edge and small-tile kernels: tiles that may cross N or M_pad, and split-K.
+//
+// With s = 1 workgroup w computes tile t (XCD-aware, see tile_of_workgroup)
+// over all of K.  Shapes with too few tiles to keep the CUs busy (small M,
+// narrow N) split K into s chunks of whole 256-byte pairs: XCD x owns a
+// contiguous range of tiles and its workgroups take them chunk by chunk, so
+// the s chunks of a tile run on one XCD.  Each chunk stores its raw partial
+// sum in the tile's slot of the workspace (thread-major float4 blocks: block
+// b of thread t at float4 index b*NT + t), counts itself in, and the last to
+// arrive adds the s partials in chunk order (so the sum does not depend on
+// the arrival order) and writes the output.  No workgroup waits for another.
+// ---------------------------------------------------------------------------
+struct SplitK {
+    int s;          // K chunks per tile (1: no split)
+    int pairs;      // K / 256
+    float* part;    // s partial slots per tile
+    unsigned* cnt;  // arrival counter per tile
+};
+
+// Tile and K chunk of workgroup w among T tiles; false if w has no work.
+__device__ __forceinline__ bool tile_of_workgroup(int w, int T, const SplitK& S, int& t, int& chunk) {
+    const int tall = T / kXcds, rem = T % kXcds;
+    const int x = w % kXcds, j = w / kXcds;
+    const int first = x * tall + (x < rem ? x : rem);
+    if (S.s <= 1) {
+        t = first + j;
+        chunk = 0;
+        return true;
+    }
+    const int count = tall + (x < rem ? 1 : 0);
+    const int tl = j / S.s;
+    chunk = j % S.s;
+    t = first + tl;
+    return tl < count;
+}
+
+// Split-K epilogue for a TN x TM wave tile of NT threads: store this chunk's
+// partial, count in; the last chunk returns true with acc = the sum of the s
+// partials in chunk order (read 4 chunks per batch, without this CU's L1).
+template <int TN, int TM, int NT>
+__device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& S, int t, int chunk,
+                                             unsigned& arrival, int tid) {
+    constexpr int NB = TN * TM * 4;  // float4 blocks per thread
+    constexpr uint32_t kSlot = NB * NT * 16u;  // bytes per slot
+    float* slots = S.part + (size_t)t * S.s * (kSlot / 4);
+    float4* mine = reinterpret_cast<float4*>(slots + (size_t)chunk * (kSlot / 4));
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                mine[((i * TM + j) * 4 + g) * NT + tid] =
+                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    // all chunks of this tile run on this XCD, whose L2 is coherent for its
+    // CUs: wait until the stores have reached it, then count in
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) arrival = __hip_atomic_fetch_add(S.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != (unsigned)(S.s - 1)) return false;
+    if (tid == 0) __hip_atomic_store(S.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+    const __amdgpu_buffer_rsrc_t prs =
+        tile_rsrc(reinterpret_cast<const uint8_t*>(slots), (uint32_t)S.s * kSlot);
+    const __amdgpu_buffer_rsrc_t zr = tile_rsrc(nullptr, 0u);
+    for (int c0 = 0; c0 < S.s; c0 += 4) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)  // chunks past s read as zero (range-0 resource) and are skipped
+                v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     c0 + u < S.s ? prs : zr,
+                                                     (uint32_t)(c0 + u) * kSlot + (uint32_t)(b * NT + tid) * 16u, 0, 1));
+            const int i = b / (TM * 4), j = (b / 4) % TM, g = b % 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float sum = c0 == 0 ? __uint_as_float(v[0][e]) : acc[i][j][4 * g + e] + __uint_as_float(v[0][e]);
+#pragma unroll
+                for (int u = 1; u < 4; ++u)
+                    if (c0 + u < S.s) sum += __uint_as_float(v[u][e]);
+                acc[i][j][4 * g + e] = sum;
+            }
+        }
+    }
+    return true;
+}
+
+template <int BN, int BM, int WN, int WM, bool kSplit>
 __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
     int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
-    int tiles_n, int group_m) {
+    int tiles_n, int group_m, SplitK S) {
     constexpr int NT = 64 * WN * WM;
     constexpr int WTN = BN / WN, WTM = BM / WM;
     constexpr int TN = WTN / 32, TM = WTM / 32;
@@ -464,19 +543,14 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     static_assert((BN * 8) % NT == 0 && (BM * 8) % NT == 0, "stage load must split evenly");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BN + BM) * kBK];
+    __shared__ unsigned arrival;
 
-    const int T = tiles_m * tiles_n;
-    const int w = blockIdx.x;
-    const int tall = T / kXcds, rem = T % kXcds;
-    const int x = w % kXcds, loc = w / kXcds;
-    const int t = x * tall + (x < rem ? x : rem) + loc;
-    const int per_group = group_m * tiles_n;
-    const int gidx = t / per_group;
-    const int first_m = gidx * group_m;
-    const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int tin = t - gidx * per_group;
-    const int n0 = (tin / gm) * BN;
-    const int m0 = (first_m + tin % gm) * BM;
+    int t, chunk;
+    if (!tile_of_workgroup(blockIdx.x, tiles_m * tiles_n, S, t, chunk)) return;
+    int n0, m0;
+    grouped_origin_bb<BN, BM>(t, tiles_m, tiles_n, group_m, n0, m0);
+    const int p0 = chunk * S.pairs / S.s, p1 = (chunk + 1) * S.pairs / S.s;
+    const int k0 = 2 * p0, KT = 2 * (p1 - p0);  // K-steps of 128 bytes: [k0, k0 + KT)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -494,7 +568,6 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     // has two steps of MFMA work to land.  Two LDS stages.  K/128 is even (K is
     // a multiple of 256), so the loop is unrolled by two and the register sets
     // are static.
-    const int KT = K / kBK;
     const bool edge = (n0 + BN > N) || (m0 + BM > Mp);
     const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(Wt + (size_t)n0 * K, (uint32_t)BN * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t ars = tile_rsrc(A + (size_t)m0 * K, (uint32_t)BM * (uint32_t)K);
@@ -511,18 +584,18 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
             load_buf<LA, NT>(RA, ars, voff, (KB), step);                 \
         }                                                                \
     } while (0)
-    RZ_STAGE_LOAD(rw0, ra0, 0);
-    RZ_STAGE_LOAD(rw1, ra1, kBK);
+    RZ_STAGE_LOAD(rw0, ra0, k0 * kBK);
+    RZ_STAGE_LOAD(rw1, ra1, (k0 + 1) * kBK);
     store_rows<LW, NT>(smem[0], rw0, tid);
     store_rows<LA, NT>(smem[0] + BN * kBK, ra0, tid);
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
-        if (kt + 2 < KT) RZ_STAGE_LOAD(rw0, ra0, (kt + 2) * kBK);
+        if (kt + 2 < KT) RZ_STAGE_LOAD(rw0, ra0, (k0 + kt + 2) * kBK);
         mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[0], wn, wm, lane);
         store_rows<LW, NT>(smem[1], rw1, tid);
         store_rows<LA, NT>(smem[1] + BN * kBK, ra1, tid);
         __syncthreads();
-        if (kt + 3 < KT) RZ_STAGE_LOAD(rw1, ra1, (kt + 3) * kBK);
+        if (kt + 3 < KT) RZ_STAGE_LOAD(rw1, ra1, (k0 + kt + 3) * kBK);
         mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[1], wn, wm, lane);
         if (kt + 2 < KT) {
             store_rows<LW, NT>(smem[0], rw0, tid);
@@ -532,6 +605,8 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     }
 #undef RZ_STAGE_LOAD
 
+    if constexpr (kSplit)  // (the 256x256 instance never splits: its registers are full)
+        if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
     const float s = act_scale[1] * w_scale;
     const bool vec = (N & 3) == 0;
 #pragma unroll
@@ -563,7 +638,7 @@ template <int BN, int BM, int WN, int WM>
 __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
     int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
-    int tiles_n, int group_m) {
+    int tiles_n, int group_m, SplitK S) {
     constexpr int NT = 64 * WN * WM;
     constexpr int WTN = BN / WN, WTM = BM / WM;
     constexpr int TN = WTN / 32, TM = WTM / 32;
@@ -572,20 +647,15 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     static_assert((BN * 8) % NT == 0 && (BM * 8) % NT == 0, "stage load must split evenly");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BN + BM) * kBK];
+    __shared__ unsigned arrival;
 
     // ---- tile mapping
-    const int T = tiles_m * tiles_n;
-    const int w = blockIdx.x;
-    const int tall = T / kXcds, rem = T % kXcds;
-    const int x = w % kXcds, loc = w / kXcds;
-    const int t = x * tall + (x < rem ? x : rem) + loc;
-    const int per_group = group_m * tiles_n;
-    const int gidx = t / per_group;
-    const int first_m = gidx * group_m;
-    const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int tin = t - gidx * per_group;
-    const int n0 = (tin / gm) * BN;
-    const int m0 = (first_m + tin % gm) * BM;
+    int t, chunk;
+    if (!tile_of_workgroup(blockIdx.x, tiles_m * tiles_n, S, t, chunk)) return;
+    int n0, m0;
+    grouped_origin_bb<BN, BM>(t, tiles_m, tiles_n, group_m, n0, m0);
+    const int p0 = chunk * S.pairs / S.s, p1 = (chunk + 1) * S.pairs / S.s;
+    const int k0 = 2 * p0;  // first K-step of 128 bytes
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -599,11 +669,11 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
         for (int j = 0; j < TM; ++j) acc[i][j] = (v16f){};
 
     u32x4 rw[LW], ra[LA];
-    const int KT = K / kBK;
+    const int KT = 2 * (p1 - p0);
 
     // prologue: stage 0
-    load_rows<LW, NT>(rw, Wt, n0, N, K, 0, tid);
-    load_rows<LA, NT>(ra, A, m0, Mp, K, 0, tid);
+    load_rows<LW, NT>(rw, Wt, n0, N, K, k0 * kBK, tid);
+    load_rows<LA, NT>(ra, A, m0, Mp, K, k0 * kBK, tid);
     store_rows<LW, NT>(smem[0], rw, tid);
     store_rows<LA, NT>(smem[0] + BN * kBK, ra, tid);
     __syncthreads();
@@ -611,8 +681,8 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + 1 < KT;
         if (more) {
-            load_rows<LW, NT>(rw, Wt, n0, N, K, (kt + 1) * kBK, tid);
-            load_rows<LA, NT>(ra, A, m0, Mp, K, (kt + 1) * kBK, tid);
+            load_rows<LW, NT>(rw, Wt, n0, N, K, (k0 + kt + 1) * kBK, tid);
+            load_rows<LA, NT>(ra, A, m0, Mp, K, (k0 + kt + 1) * kBK, tid);
         }
         const uint8_t* sw = smem[kt & 1];
         const uint8_t* sa = smem[kt & 1] + BN * kBK;
@@ -639,6 +709,7 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     }
 
     // ---- epilogue: y = acc * (s_act * s_w), fp32 row-major
+    if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
     const float s = act_scale[1] * w_scale;
     const bool vec = (N & 3) == 0;
 #pragma unroll
@@ -675,23 +746,45 @@ constexpr KindInfo kKinds[4] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128},
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+
 // Arrival counters of the split tiles (one uint32 each), padded to 256 bytes;
 // the partial sums follow.
 size_t split_counter_bytes(int rem) { return ((size_t)rem * sizeof(unsigned) + 255) / 256 * 256; }
 
+// K chunks per tile for the edge-capable kinds.  The 128x128 kernel (two
+// workgroups per CU) splits until the chunks fill one workgroup per CU, in
+// chunks of >= 2 K pairs; the 64x32 kernel, which is memory-bound, until
+// there are about two workgroups per CU, in chunks of >= 1 pair.  The
+// 256x256 edge kernel only runs with >= 256 tiles and never splits.
+int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
+    const int pairs = (int)(k / 256u);
+    int s = 1;
+    if (kind == kMedium) {
+        const int T = ceil_div(mp, 128) * ceil_div((int)n, 128);
+        s = 256 / T < pairs / 2 ? 256 / T : pairs / 2;
+    } else if (kind == kSmall) {
+        const int T = ceil_div(mp, 32) * ceil_div((int)n, 64);
+        s = 512 / T < pairs ? 512 / T : pairs;
+    }
+    return s < 1 ? 1 : s;
+}
+
 }  // namespace
 
 // Kernel choice per shape:
-//  * interior 256x256 tiles (tile kernel, plus the split kernel for the
-//    last partial round) when N and padded M are multiples of 256,
-//    K >= 512, N <= 2^21 and there are at least 64 tiles;
+//  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
+//    as half tiles when they fit one round) when N and padded M are
+//    multiples of 256, K >= 512, N <= 2^21 and there are at least 64 tiles;
 //  * 256x256 edge-capable kernel when tiles cross N or padded M but there are
 //    still >= 256 of them;
-//  * 128x128 tiles when that gives >= 256 tiles;
+//  * 128x128 tiles when M_pad >= 128 and tiles times K chunks give >= 128
+//    workgroups;
 //  * 64x32 tiles otherwise (small M, few tiles).
+// The last two split K (edge_split) when a workspace is given.
 GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed) {
     const int mp = (int)((m + 15u) & ~15u);
     GemmPlan p = {};
+    p.s = 1;
     const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
     if (mp % 256 == 0 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
         p.kind = kTiles;
@@ -701,18 +794,9 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
         // the whole-tile rounds must be whole n-columns of tiles
         if ((p.R * cus) % tiles_m != 0) p.R = 0;
         p.rem = t256 - p.R * cus;
-        p.s = 1;
-        const int pairs = (int)(k / 256u);
-        const int per_xcd = ceil_div(p.rem, kXcds);
-        if (p.rem > 0 && p.rem <= cus && split_allowed) {
-            int s = (cus / kXcds) / per_xcd;
-            s = s < 1 ? 1 : (s > 2 ? 2 : s);
-            p.s = s > pairs / 2 ? pairs / 2 : s;  // chunks of >= 2 pairs (>= 4 K-steps)
-        }
-        if (p.s > 1) {
+        if (p.rem > 0 && 2 * p.rem <= cus) {  // last round in half tiles
             p.workgroups = p.R * cus;
-            p.split_workgroups = kXcds * per_xcd * p.s;
-            p.ws_bytes = split_counter_bytes(p.rem) + (size_t)p.rem * p.s * 256 * 256 * sizeof(float);
+            p.half_workgroups = kXcds * ceil_div(2 * p.rem, kXcds);
         } else {  // every tile whole
             p.R = t256 / cus;
             p.rem = 0;
@@ -720,7 +804,7 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
         }
     } else if (t256 >= 256) {
         p.kind = kLargeEdge;
-    } else if (mp >= 128 && ceil_div(mp, 128) * ceil_div((int)n, 128) >= 256) {
+    } else if (mp >= 128 && ceil_div(mp, 128) * ceil_div((int)n, 128) * edge_split(kMedium, mp, n, k) >= 128) {
         p.kind = kMedium;
     } else {
         p.kind = kSmall;
@@ -728,7 +812,16 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     p.bn = kKinds[p.kind].bn;
     p.bm = kKinds[p.kind].bm;
     p.threads = kKinds[p.kind].threads;
-    if (p.kind != kTiles) p.workgroups = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
+    if (p.kind != kTiles) {
+        const int T = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
+        p.workgroups = T;
+        p.s = split_allowed ? edge_split(p.kind, mp, n, k) : 1;
+        if (p.s > 1) {  // XCD x runs the chunks of its own tiles (tile_of_workgroup)
+            p.rem = T;
+            p.workgroups = kXcds * ceil_div(T, kXcds) * p.s;
+            p.ws_bytes = split_counter_bytes(T) + (size_t)T * p.s * p.bn * p.bm * sizeof(float);
+        }
+    }
     return p;
 }
 
@@ -736,46 +829,46 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
                        uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
                        size_t ws_bytes, int cus, hipStream_t st) {
     GemmPlan p = plan_gemm(m, n, k, cus, true);
-    if (p.kind == kTiles && p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
+    if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
         p = plan_gemm(m, n, k, cus, false);  // no room for partial sums: whole tiles only
     const int mp = (int)((m + 15u) & ~15u);
     const int tiles_m = ceil_div(mp, p.bm), tiles_n = ceil_div((int)n, p.bn);
     const int group_m = tiles_m < 8 ? tiles_m : 8;
+    SplitK S = {1, (int)(k / 256u), nullptr, nullptr};
+    if (p.kind != kTiles && p.s > 1) {
+        S.s = p.s;
+        S.cnt = static_cast<unsigned*>(ws);
+        S.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem));
+    }
     switch (p.kind) {
         case kTiles: {
             InteriorPlan ip;
             ip.tiles_m = tiles_m;
-            ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without a split)
+            ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
             ip.nd = p.workgroups / tiles_m;
             ip.group_m = group_m;
-            ip.rem = p.s > 1 ? p.rem : 0;
-            ip.per_xcd = ceil_div(ip.rem, kXcds);
-            // groups of ~sqrt(tiles per XCD) m-tiles: each XCD's block of split tiles is near square
-            int tgm = 1;
-            while (tgm * 2 <= tiles_m && tgm * tgm * 4 <= ip.per_xcd) tgm *= 2;
-            ip.tail_gm = tgm;
-            ip.s = p.s;
-            ip.pairs = (int)(k / 256u);
-            unsigned* cnt = p.s > 1 ? static_cast<unsigned*>(ws) : nullptr;
-            float* part = p.s > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem))
-                                  : nullptr;
-            const int grid = p.workgroups + (p.s > 1 ? p.split_workgroups : 0);
-            fp8_gemm_interior_kernel<<<grid, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale, w_scale,
-                                                           ip, part, cnt);
-            (void)tiles_n;
+            ip.nhalf = 2 * p.rem;
+            // groups of about sqrt(2 * halves per XCD) halves: each XCD's block
+            // of half tiles is near square in elements
+            const int per_xcd = ceil_div(ip.nhalf, kXcds);
+            int hgm = 1;
+            while (hgm * 2 <= 2 * tiles_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
+            ip.half_gm = hgm;
+            fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(
+                a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale, w_scale, ip);
             break;
         }
         case kLargeEdge:
-            fp8_gemm_deep_kernel<256, 256, 2, 2><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
+            fp8_gemm_deep_kernel<256, 256, 2, 2, false><<<p.workgroups, p.threads, 0, st>>>(
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
             break;
         case kMedium:
-            fp8_gemm_deep_kernel<128, 128, 2, 2><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
+            fp8_gemm_deep_kernel<128, 128, 2, 2, true><<<p.workgroups, p.threads, 0, st>>>(
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
             break;
         default:
             fp8_gemm_kernel<64, 32, 2, 1><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m);
+                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
             break;
     }
     return hipGetLastError();

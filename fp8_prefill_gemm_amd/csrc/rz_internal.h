@@ -34,9 +34,11 @@ hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hi
 // ---- gemm.hip
 struct GemmPlan {
     int bn, bm, threads, workgroups, kind;
-    // interior-tile plan: CUs, whole-tile rounds, split tiles, K chunks per
-    // split tile, workgroups of the split kernel
-    int G, R, rem, s, split_workgroups;
+    // interior-tile plan: CUs, whole-tile rounds, tiles left over (run as
+    // half tiles), workgroups for those half tiles
+    int G, R, rem, half_workgroups;
+    // edge-capable plans: K chunks per tile (1: no split)
+    int s;
     size_t ws_bytes;  // workspace the plan needs (0: none)
 };
 GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed);

@@ -115,12 +115,14 @@ def test_gemm_validation(L):
 
 
 def test_gemm_workspace_sizes(L):
-    # split-K workspace only for persistent plans whose last round is split
-    assert L.rz_fp8_gemm_workspace_bytes(16, 256, 512) == 0
+    # split-K workspace: 256 bytes of arrival counters + 4 tiles x 2 chunks of 64x32 fp32
+    assert L.rz_fp8_gemm_workspace_bytes(16, 256, 512) == 256 + 4 * 2 * 64 * 32 * 4
     assert L.rz_fp8_gemm_workspace_bytes(0, 256, 512) == 0
     assert L.rz_fp8_gemm_workspace_bytes(2048, 256, 300) == 0
-    big = L.rz_fp8_gemm_workspace_bytes(2048, 18944, 3584)
-    assert big > 0 and big % 16 == 0
+    # interior-tile plans need none; the 128x128 split needs counters + 2 chunks of 112 tiles
+    assert L.rz_fp8_gemm_workspace_bytes(2048, 18944, 3584) == 0
+    assert L.rz_fp8_gemm_workspace_bytes(2048, 3584, 18944) == 0
+    assert L.rz_fp8_gemm_workspace_bytes(512, 3584, 3584) == 512 + 112 * 2 * 128 * 128 * 4
 
 
 def test_diagnostics_validation(L):
@@ -150,32 +152,65 @@ def test_plans_cover_shapes(L):
         mp = rz.rz_pad_m(m)
         tiles = -(-mp // bm) * -(-n // bn)
         interior = (bn, bm) == (256, 256) and mp % 256 == 0 and n % 256 == 0 and k >= 512 and tiles >= 64
-        assert wgs == (_interior_wgs(mp // 256, n // 256, k) if interior else tiles)
+        if interior:
+            assert wgs == _interior_wgs(mp // 256, n // 256, k)
+        else:
+            assert (bn, bm, wgs) == _edge_plan(m, n, k)[:3]
+            assert wgs >= tiles
         assert threads in (64, 128, 256, 512)
+
+
+def _edge_plan(m, n, k, cus=256):
+    """(BN, BM, workgroups, workspace bytes) of a plan that is not interior
+    (256 CUs): 256x256 tiles from 256 tiles on, unsplit; else 128x128 tiles
+    split into s = min(256 // tiles, pairs // 2) K chunks if M_pad >= 128 and
+    that gives >= 128 workgroups; else 64x32 tiles in s = min(512 // tiles,
+    pairs) chunks.  A split rounds the tiles up to a multiple of 8 (XCDs)."""
+    mp = -(-m // 16) * 16
+    pairs = k // 256
+
+    def tiles(bn, bm):
+        return -(-mp // bm) * -(-n // bn)
+
+    if tiles(256, 256) >= 256:
+        return 256, 256, tiles(256, 256), 0
+    t = tiles(128, 128)
+    s = max(1, min(256 // t, pairs // 2))
+    if mp >= 128 and t * s >= 128:
+        bn, bm = 128, 128
+    else:
+        bn, bm = 64, 32
+        t = tiles(64, 32)
+        s = max(1, min(512 // t, pairs))
+    if s == 1:
+        return bn, bm, t, 0
+    return bn, bm, 8 * -(-t // 8) * s, -(-4 * t // 256) * 256 + t * s * bn * bm * 4
 
 
 def _interior_wgs(tiles_m, tiles_n, k, cus=256):
     """Workgroups of an interior-tile plan (256 CUs without a device): whole
-    tiles for the full rounds, then the leftover tiles split along K into s
-    chunks per tile (s <= 2, s*leftover <= CUs, chunks of >= 2 K pairs), or
-    every tile whole when no split fits."""
+    tiles for the full rounds (whole n-columns of tiles, else none), then the
+    leftover tiles as two half tiles each when they fit one round (rounded up
+    to a multiple of 8 XCDs), or every tile whole."""
     t = tiles_m * tiles_n
     r = t // cus
     if (r * cus) % tiles_m:
         r = 0
     rem = t - r * cus
-    per_xcd = -(-rem // 8)
-    s = min(2, max(1, (cus // 8) // per_xcd), (k // 256) // 2) if 0 < rem <= cus else 1
-    return r * cus + 8 * per_xcd * s if s > 1 else t
+    if 0 < rem and 2 * rem <= cus:
+        return r * cus + 8 * -(-2 * rem // 8)
+    return t
 
 
 def test_interior_plan_examples(L):
-    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles in 2 K chunks
+    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles as 160 half tiles
     assert rz.rz_fp8_gemm_plan(2048, 18944, 3584)[3] == 512 + 160
-    # FFN down at M=2048: 112 tiles, all split in 2 K chunks
+    # FFN down at M=2048: 112 tiles, all as 224 half tiles
     assert rz.rz_fp8_gemm_plan(2048, 3584, 18944)[3] == 224
-    # M=4096: 1184 tiles, 160 left over is too many to split: all whole
+    # M=4096: 1184 tiles, the 160 left over make 320 halves, more than a round: all whole
     assert rz.rz_fp8_gemm_plan(4096, 18944, 3584)[3] == 1184
+    # 3 m-tiles: 256-tile rounds are not whole n-columns, 300 tiles all whole
+    assert rz.rz_fp8_gemm_plan(768, 25600, 512)[3] == 300
 
 
 def test_binding_refuses_host_tensors(L):

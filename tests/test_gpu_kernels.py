@@ -265,34 +265,71 @@ def _codes(g, shape):
 
 
 @pytest.mark.parametrize("m,n,k,full", [
-    (2048, 2560, 1536, True),    # 80 tiles: all split in 2 K chunks of 3 pairs
-    (2048, 2560, 2816, False),   # 80 tiles in 2 uneven chunks (5, 6 pairs)
-    (2048, 2560, 768, True),     # 80 tiles, K too short to split: whole tiles
-    (2048, 3584, 1024, True),    # 112 tiles: all split in 2 chunks of 2 pairs
-    (2048, 10240, 1024, False),  # 320 tiles: one whole round + 64 tiles split in 2
+    (2048, 2560, 1536, True),    # 80 tiles: all as 160 half tiles
+    (2040, 2560, 1024, True),    # same with M padded to 2048: rows >= M dropped
+    (2048, 2560, 768, True),     # 80 tiles as half tiles, 6 K-steps
+    (2048, 3584, 1024, True),    # 112 tiles: 224 half tiles
+    (2048, 10240, 1024, False),  # 320 tiles: one whole round + 64 tiles as halves
+    (2048, 8960, 512, False),    # 280 tiles: one whole round + 24 tiles as halves
     (4096, 4096, 512, False),    # 256 tiles: exactly one round
-    (4096, 4608, 1024, False),   # 288 tiles: one round + 32 split tiles
+    (4096, 4608, 1024, False),   # 288 tiles: one round + 32 tiles as halves
+    (768, 25600, 512, False),    # 300 tiles, rounds not whole n-columns: all whole
+    (2040, 3584, 4864, False),   # 112 tiles as half tiles with long K, rows >= M dropped
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
+    from tests.test_abi import _interior_wgs
+    mp = fp8_path.pad_m(m)
     bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
     assert (bn, bm, threads) == (256, 256, 256)
+    assert wgs == _interior_wgs(mp // 256, n // 256, k)
+    assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
     g = np.random.Generator(np.random.PCG64(m + n + k))
-    a8, w8 = _codes(g, (m, k)), _codes(g, (n, k))
+    a8, w8 = _codes(g, (mp, k)), _codes(g, (n, k))
+    a8[m:] = 0
     sc = np.array([1.0, 0.03, 0, 0], np.float32)
     wdq = np.float32(0.011)
     A, Wd, S = dev(a8), dev(w8), dev(sc)
     rows = np.arange(m) if full else np.unique(np.concatenate([[0, 1, m - 1], g.choice(m, 61, replace=False)]))
     yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
-    need = rz.rz_fp8_gemm_workspace_bytes(m, n, k)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
-    # with the workspace (split tail) twice in a row, then without (whole tiles)
+    for _ in range(2):  # twice in a row: nothing carried over between calls
+        y = host(rz.rz_fp8_gemm(A, Wd, m, S, float(wdq)))
+        assert y.shape == (m, n)
+        err = np.abs(y[rows].astype(np.float64) - yr)
+        assert (err <= tol).all(), f"{(err > tol).sum()} out of bound"
+
+
+@pytest.mark.parametrize("m,n,k,full", [
+    (4, 200, 768, True),       # 64x32 tiles, 3 K chunks of 1 pair, ragged n
+    (37, 200, 2816, True),     # 64x32 tiles, 11 chunks, ragged m and n
+    (1, 4608, 3584, True),     # 64x32 tiles, 7 chunks of 2 pairs
+    (300, 520, 2048, True),    # 64x32 tiles, 5 uneven chunks
+    (600, 1000, 3584, False),  # 128x128 tiles, 6 uneven chunks, ragged m and n
+    (512, 3584, 3584, False),  # 128x128 tiles in 2 chunks
+    (4096, 512, 3584, False),  # 128x128 tiles in 2 chunks
+])
+def test_gemm_edge_split_plans(rz, m, n, k, full):
+    from tests.test_abi import _edge_plan
+    bn, bm, wgs, need = _edge_plan(m, n, k)
+    assert rz.rz_fp8_gemm_plan(m, n, k)[:2] == (bn, bm) and rz.rz_fp8_gemm_plan(m, n, k)[3] == wgs
+    assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == need > 0
+    g = np.random.Generator(np.random.PCG64(m * 3 + n + k))
+    mp = fp8_path.pad_m(m)
+    a8 = _codes(g, (mp, k))
+    a8[m:] = 0
+    w8 = _codes(g, (n, k))
+    sc = np.array([1.0, 0.021, 0, 0], np.float32)
+    wdq = np.float32(0.0093)
+    A, Wd, S = dev(a8), dev(w8), dev(sc)
+    rows = np.arange(m) if full else np.unique(np.concatenate([[0, 1, m - 1], g.choice(m, 45, replace=False)]))
+    yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    # split K twice in a row on one workspace, then whole tiles without one
     for use_ws in (ws, ws, None):
         y = host(rz.rz_fp8_gemm(A, Wd, m, S, float(wdq), ws=use_ws))
         err = np.abs(y[rows].astype(np.float64) - yr)
         assert (err <= tol).all(), f"{(err > tol).sum()} out of bound (ws={use_ws is not None})"
-    if need:
-        rem = (m // 256) * (n // 256) % 256
-        assert (host(ws[:4 * rem]) == 0).all()  # arrival counters left at zero for the next call
+    tiles = -(-mp // bm) * -(-n // bn)
+    assert (host(ws[:4 * tiles]) == 0).all()  # arrival counters left at zero for the next call
 
 
 def test_gemm_identity_weight(rz):
