@@ -127,10 +127,11 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
  *   ws, ws_bytes  optional device workspace (may be NULL / 0) of at least
  *                 rz_fp8_gemm_workspace_bytes(m, n, k) bytes, zero-filled
  *                 before its first use; every call leaves it reusable.  It
- *                 holds partial sums when the last round of output tiles is
- *                 split along K to keep every compute unit busy; without it
- *                 (or when it is too small) that round runs unsplit.  Calls
- *                 that share a workspace must be ordered (same stream).
+ *                 holds partial sums and arrival counters when a shape with
+ *                 few output tiles (small or medium m, narrow n) splits K
+ *                 to keep the compute units busy; without it (or when it is
+ *                 too small) every tile runs over the whole K.  Calls that
+ *                 share a workspace must be ordered (same stream).
  * Products are accumulated in fp32 on the matrix cores (no fp16 stage); the
  * summation order may differ between calls with and without a workspace.
  * k <= RZ_MAX_GEMM_K.  m == 0 or n == 0 is a no-op (any pointer may then
@@ -175,8 +176,8 @@ int rz_fp8_scales(const float* absmax_dev, uint64_t count, float* q_out_dev,
 
 /* GEMM tile configuration rz_fp8_gemm would launch for this shape (with a
  * large enough workspace): writes {BN, BM, threads, workgroups} to
- * cfg_out[4] (host); workgroups counts every launch of the call (whole
- * tiles plus K chunks of split tiles). */
+ * cfg_out[4] (host); workgroups is the grid of the one launch: whole tiles
+ * plus half tiles, or tiles times K chunks when K is split. */
 int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out);
 
 const char* rz_status_string(int status);
