@@ -35,7 +35,7 @@ METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "rz_device.h")]
+                  for f in ("gemm.hip", "gemm_common.h", "rz_internal.h")]
 
 
 def log(*a):

@@ -19,130 +19,22 @@
 // lane ends with runs of 4 consecutive n of one output row m: 16-byte stores
 // into the row-major fp32 output.
 //
-// A workgroup owns a BN x BM output tile and walks K in steps of 128 bytes
-// with two LDS stages: the next step's global loads are issued before the
-// current step's MFMAs and written to the other stage afterwards (one
-// barrier per step).  LDS rows are 128 bytes; the 16-byte chunk c of row r
-// is stored at c ^ ((r ^ r>>3) & 7) so that the MFMA operand reads (8 or 16
-// consecutive rows, same chunk) and the stage writes hit distinct banks.
+// This file: the 256x256 interior-tile kernel (the large prefill GEMMs),
+// the plan that picks a kernel per shape, and the launcher.  Kernels for
+// tiles that cross N or padded M, small M and few tiles are in
+// gemm_edge.hip.
 //
 // Workgroup -> tile mapping is XCD-aware: the dispatcher sends workgroup w
 // to XCD w % 8, so w is first remapped to a contiguous range of tiles per
 // XCD; inside it tiles go m-fastest within groups of `group_m` m-tiles, so
 // the workgroups that run together on one XCD share weight rows and
 // activation rows through that XCD's L2.
-#include "rz_device.h"
+#include "gemm_common.h"
 #include "rz_internal.h"
 
 namespace rz {
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-// Native 16-byte vector for staging: plain loads/stores (HIP's uint4 is a
-// class whose copies become memcpy and keep the staging arrays in memory).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kBK = 128;
-constexpr int kXcds = 8;
-
-// 16-byte chunk swizzle of a 128-byte LDS row.  It depends only on row bits
-// 0..4, so rows r and r + 32i share it (the per-thread LDS addresses of a
-// stage then differ by immediates), and any 8 consecutive rows starting at
-// a multiple of 8 (or 16 starting at a multiple of 16) hit distinct banks.
-__device__ __forceinline__ int swz(int row) { return ((row ^ (row >> 3)) & 3) ^ (row & 4); }
-
-// Global -> registers: L x 16 bytes per thread of a [rows][128-byte] K-slice
-// starting at column kb; rows at or past `limit` read as zero.
-template <int L, int NT>
-__device__ __forceinline__ void load_rows(u32x4 (&r)[L], const uint8_t* __restrict__ src, int row0,
-                                          int limit, int K, int kb, int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int idx = tid + i * NT;
-        const int gr = row0 + (idx >> 3);
-        u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-        if (gr < limit) v = *reinterpret_cast<const u32x4*>(src + (size_t)gr * K + kb + ((idx & 7) << 4));
-        r[i] = v;
-    }
-}
-
-// Registers -> one LDS stage (128-byte rows, XOR-swizzled 16-byte chunks).
-template <int L, int NT>
-__device__ __forceinline__ void store_rows(uint8_t* dst, const u32x4 (&r)[L], int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int idx = tid + i * NT;
-        const int row = idx >> 3;
-        *reinterpret_cast<u32x4*>(dst + row * kBK + (((idx & 7) ^ swz(row)) << 4)) = r[i];
-    }
-}
-
-// One 32-byte MFMA operand: row `row`, chunks c0 and c0+1 of a stage.
-__device__ __forceinline__ v8i frag(const uint8_t* base, int row, int c0) {
-    const uint8_t* r = base + row * kBK;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + ((c0 ^ swz(row)) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + (((c0 + 1) ^ swz(row)) << 4));
-    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Global -> registers for one operand of a stage: thread `tid` moves the
-// 16-byte chunk (tid & 7) of rows (tid >> 3) + (NT/8)*i, i < L.  Buffer loads
-// keep the addressing in one per-lane 32-bit offset (`voff` = (tid >> 3) * K
-// + 16 * (tid & 7)) plus a uniform scalar offset (the stage's K offset plus
-// i rows-steps), so no per-load 64-bit address stays live in VGPRs.  `rsrc`
-// covers the tile's rows from its first row; the caller keeps every offset
-// below 2^32 (K < 2^24).
-template <int L, int NT>
-__device__ __forceinline__ void load_buf(u32x4 (&r)[L], __amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
-                                         uint32_t kb, uint32_t step) {
-#pragma unroll
-    for (int i = 0; i < L; ++i)
-        r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, kb + i * step, 0));
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, uint32_t bytes) {
-    // gfx9-family raw buffer: stride 0, range `bytes`, default data format word
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Edge tiles: rows at or past `limit` are clamped to the last valid row
-// (their products only reach outputs that are never stored).
-template <int L, int NT>
-__device__ __forceinline__ void load_clamped(u32x4 (&r)[L], const uint8_t* __restrict__ src, int row0,
-                                             int limit, int K, int kb, int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        int gr = row0 + (tid >> 3) + (NT / 8) * i;
-        gr = gr < limit ? gr : limit - 1;
-        r[i] = *reinterpret_cast<const u32x4*>(src + (size_t)gr * K + kb + 16 * (tid & 7));
-    }
-}
-
-// All MFMAs of one 128-byte K-step for one wave: for each 64-byte half, the
-// wave's TN weight fragments stay in registers while its TM activation
-// fragments are read one at a time.
-template <int BN, int WTN, int WTM, int TN, int TM>
-__device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* stage, int wn, int wm,
-                                          int lane) {
-    const uint8_t* sw = stage;
-    const uint8_t* sa = stage + BN * kBK;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int c0 = kk * 4 + (lane >> 5) * 2;
-        v8i af[TN];
-#pragma unroll
-        for (int i = 0; i < TN; ++i) af[i] = frag(sw, wn * WTN + i * 32 + (lane & 31), c0);
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const v8i bf = frag(sa, wm * WTM + j * 32 + (lane & 31), c0);
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf, acc[i][j], 0, 0,
-                                                                            0, 0, 0, 0);
-        }
-    }
-}
+using namespace gemm;
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
@@ -289,18 +181,6 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
 // ahead of the MFMAs in two register sets.
 // ---------------------------------------------------------------------------
 
-// Origin of tile t of BN x BM tiles in the grouped order of a tiles_m x
-// tiles_n region (groups of gm m-tiles, m fastest inside a group).
-template <int BN, int BM>
-__device__ __forceinline__ void grouped_origin_bb(int t, int tiles_m, int tiles_n, int gm_full, int& n0, int& m0) {
-    const int per_group = gm_full * tiles_n;
-    const int gidx = t / per_group;
-    const int first_m = gidx * gm_full;
-    const int gm = (tiles_m - first_m) < gm_full ? (tiles_m - first_m) : gm_full;
-    const int tin = t - gidx * per_group;
-    n0 = (tin / gm) * BN;
-    m0 = (first_m + tin % gm) * BM;
-}
 
 // acc over the K-steps [0, KS) of the 256 x 64*TM tile whose weight rows
 // start at `wrs` and activation rows at `ars` (KS even, >= 4).
@@ -441,315 +321,14 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     store_acc<2>(acc, tile_out_rsrc(Y, M, N, m0), (uint32_t)N, (uint32_t)n0, wn, wm, lane, scale);
 }
 
-// ---------------------------------------------------------------------------
-// Edge and small-tile kernels: tiles that may cross N or M_pad, and split-K.
-//
-// With s = 1 workgroup w computes tile t (XCD-aware, see tile_of_workgroup)
-// over all of K.  Shapes with too few tiles to keep the CUs busy (small M,
-// narrow N) split K into s chunks of whole 256-byte pairs: XCD x owns a
-// contiguous range of tiles and its workgroups take them chunk by chunk, so
-// the s chunks of a tile run on one XCD.  Each chunk stores its raw partial
-// sum in the tile's slot of the workspace (thread-major float4 blocks: block
-// b of thread t at float4 index b*NT + t), counts itself in, and the last to
-// arrive adds the s partials in chunk order (so the sum does not depend on
-// the arrival order) and writes the output.  No workgroup waits for another.
-// ---------------------------------------------------------------------------
-struct SplitK {
-    int s;          // K chunks per tile (1: no split)
-    int pairs;      // K / 256
-    float* part;    // s partial slots per tile
-    unsigned* cnt;  // arrival counter per tile
-};
-
-// Tile and K chunk of workgroup w among T tiles; false if w has no work.
-__device__ __forceinline__ bool tile_of_workgroup(int w, int T, const SplitK& S, int& t, int& chunk) {
-    const int tall = T / kXcds, rem = T % kXcds;
-    const int x = w % kXcds, j = w / kXcds;
-    const int first = x * tall + (x < rem ? x : rem);
-    if (S.s <= 1) {
-        t = first + j;
-        chunk = 0;
-        return true;
-    }
-    const int count = tall + (x < rem ? 1 : 0);
-    const int tl = j / S.s;
-    chunk = j % S.s;
-    t = first + tl;
-    return tl < count;
-}
-
-// Split-K epilogue for a TN x TM wave tile of NT threads: store this chunk's
-// partial, count in; the last chunk returns true with acc = the sum of the s
-// partials in chunk order (read 4 chunks per batch, without this CU's L1).
-template <int TN, int TM, int NT>
-__device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& S, int t, int chunk,
-                                             unsigned& arrival, int tid) {
-    constexpr int NB = TN * TM * 4;  // float4 blocks per thread
-    constexpr uint32_t kSlot = NB * NT * 16u;  // bytes per slot
-    float* slots = S.part + (size_t)t * S.s * (kSlot / 4);
-    float4* mine = reinterpret_cast<float4*>(slots + (size_t)chunk * (kSlot / 4));
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                mine[((i * TM + j) * 4 + g) * NT + tid] =
-                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-    // all chunks of this tile run on this XCD, whose L2 is coherent for its
-    // CUs: wait until the stores have reached it, then count in
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) arrival = __hip_atomic_fetch_add(S.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != (unsigned)(S.s - 1)) return false;
-    if (tid == 0) __hip_atomic_store(S.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
-    const __amdgpu_buffer_rsrc_t prs =
-        tile_rsrc(reinterpret_cast<const uint8_t*>(slots), (uint32_t)S.s * kSlot);
-    const __amdgpu_buffer_rsrc_t zr = tile_rsrc(nullptr, 0u);
-    for (int c0 = 0; c0 < S.s; c0 += 4) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            u32x4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)  // chunks past s read as zero (range-0 resource) and are skipped
-                v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     c0 + u < S.s ? prs : zr,
-                                                     (uint32_t)(c0 + u) * kSlot + (uint32_t)(b * NT + tid) * 16u, 0, 1));
-            const int i = b / (TM * 4), j = (b / 4) % TM, g = b % 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float sum = c0 == 0 ? __uint_as_float(v[0][e]) : acc[i][j][4 * g + e] + __uint_as_float(v[0][e]);
-#pragma unroll
-                for (int u = 1; u < 4; ++u)
-                    if (c0 + u < S.s) sum += __uint_as_float(v[u][e]);
-                acc[i][j][4 * g + e] = sum;
-            }
-        }
-    }
-    return true;
-}
-
-template <int BN, int BM, int WN, int WM, bool kSplit>
-__global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
-    int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
-    int tiles_n, int group_m, SplitK S) {
-    constexpr int NT = 64 * WN * WM;
-    constexpr int WTN = BN / WN, WTM = BM / WM;
-    constexpr int TN = WTN / 32, TM = WTM / 32;
-    constexpr int LW = BN * 8 / NT, LA = BM * 8 / NT;
-    static_assert(TN >= 1 && TM >= 1, "wave tile must hold at least one 32x32 MFMA tile");
-    static_assert((BN * 8) % NT == 0 && (BM * 8) % NT == 0, "stage load must split evenly");
-
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BN + BM) * kBK];
-    __shared__ unsigned arrival;
-
-    int t, chunk;
-    if (!tile_of_workgroup(blockIdx.x, tiles_m * tiles_n, S, t, chunk)) return;
-    int n0, m0;
-    grouped_origin_bb<BN, BM>(t, tiles_m, tiles_n, group_m, n0, m0);
-    const int p0 = chunk * S.pairs / S.s, p1 = (chunk + 1) * S.pairs / S.s;
-    const int k0 = 2 * p0, KT = 2 * (p1 - p0);  // K-steps of 128 bytes: [k0, k0 + KT)
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int wn = wid % WN, wm = wid / WN;
-
-    v16f acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = (v16f){};
-
-    // Two-deep global prefetch: the loads for K-step s+2 are issued at step s
-    // into the register set that step s-1 already wrote to LDS, so each load
-    // has two steps of MFMA work to land.  Two LDS stages.  K/128 is even (K is
-    // a multiple of 256), so the loop is unrolled by two and the register sets
-    // are static.
-    const bool edge = (n0 + BN > N) || (m0 + BM > Mp);
-    const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(Wt + (size_t)n0 * K, (uint32_t)BN * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t ars = tile_rsrc(A + (size_t)m0 * K, (uint32_t)BM * (uint32_t)K);
-    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
-    const uint32_t step = (uint32_t)(NT / 8) * (uint32_t)K;
-    u32x4 rw0[LW], ra0[LA], rw1[LW], ra1[LA];
-#define RZ_STAGE_LOAD(RW, RA, KB)                                        \
-    do {                                                                 \
-        if (edge) {                                                      \
-            load_clamped<LW, NT>(RW, Wt, n0, N, K, (KB), tid);           \
-            load_clamped<LA, NT>(RA, A, m0, Mp, K, (KB), tid);           \
-        } else {                                                         \
-            load_buf<LW, NT>(RW, wrs, voff, (KB), step);                 \
-            load_buf<LA, NT>(RA, ars, voff, (KB), step);                 \
-        }                                                                \
-    } while (0)
-    RZ_STAGE_LOAD(rw0, ra0, k0 * kBK);
-    RZ_STAGE_LOAD(rw1, ra1, (k0 + 1) * kBK);
-    store_rows<LW, NT>(smem[0], rw0, tid);
-    store_rows<LA, NT>(smem[0] + BN * kBK, ra0, tid);
-    __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-        if (kt + 2 < KT) RZ_STAGE_LOAD(rw0, ra0, (k0 + kt + 2) * kBK);
-        mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[0], wn, wm, lane);
-        store_rows<LW, NT>(smem[1], rw1, tid);
-        store_rows<LA, NT>(smem[1] + BN * kBK, ra1, tid);
-        __syncthreads();
-        if (kt + 3 < KT) RZ_STAGE_LOAD(rw1, ra1, (k0 + kt + 3) * kBK);
-        mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[1], wn, wm, lane);
-        if (kt + 2 < KT) {
-            store_rows<LW, NT>(smem[0], rw0, tid);
-            store_rows<LA, NT>(smem[0] + BN * kBK, ra0, tid);
-        }
-        __syncthreads();
-    }
-#undef RZ_STAGE_LOAD
-
-    if constexpr (kSplit)  // (the 256x256 instance never splits: its registers are full)
-        if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    const float s = act_scale[1] * w_scale;
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int m = m0 + wm * WTM + j * 32 + (lane & 31);
-            if (m >= M) continue;
-            float* yrow = Y + (size_t)m * N;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-                const float4 v = make_float4(acc[i][j][4 * g] * s, acc[i][j][4 * g + 1] * s,
-                                             acc[i][j][4 * g + 2] * s, acc[i][j][4 * g + 3] * s);
-                if (vec && n + 3 < N) {
-                    *reinterpret_cast<float4*>(yrow + n) = v;
-                } else {
-                    if (n < N) yrow[n] = v.x;
-                    if (n + 1 < N) yrow[n + 1] = v.y;
-                    if (n + 2 < N) yrow[n + 2] = v.z;
-                    if (n + 3 < N) yrow[n + 3] = v.w;
-                }
-            }
-        }
-    }
-}
-
-template <int BN, int BM, int WN, int WM>
-__global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
-    int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
-    int tiles_n, int group_m, SplitK S) {
-    constexpr int NT = 64 * WN * WM;
-    constexpr int WTN = BN / WN, WTM = BM / WM;
-    constexpr int TN = WTN / 32, TM = WTM / 32;
-    constexpr int LW = BN * 8 / NT, LA = BM * 8 / NT;
-    static_assert(TN >= 1 && TM >= 1, "wave tile must hold at least one 32x32 MFMA tile");
-    static_assert((BN * 8) % NT == 0 && (BM * 8) % NT == 0, "stage load must split evenly");
-
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BN + BM) * kBK];
-    __shared__ unsigned arrival;
-
-    // ---- tile mapping
-    int t, chunk;
-    if (!tile_of_workgroup(blockIdx.x, tiles_m * tiles_n, S, t, chunk)) return;
-    int n0, m0;
-    grouped_origin_bb<BN, BM>(t, tiles_m, tiles_n, group_m, n0, m0);
-    const int p0 = chunk * S.pairs / S.s, p1 = (chunk + 1) * S.pairs / S.s;
-    const int k0 = 2 * p0;  // first K-step of 128 bytes
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int wn = wid % WN, wm = wid / WN;
-
-    v16f acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = (v16f){};
-
-    u32x4 rw[LW], ra[LA];
-    const int KT = 2 * (p1 - p0);
-
-    // prologue: stage 0
-    load_rows<LW, NT>(rw, Wt, n0, N, K, k0 * kBK, tid);
-    load_rows<LA, NT>(ra, A, m0, Mp, K, k0 * kBK, tid);
-    store_rows<LW, NT>(smem[0], rw, tid);
-    store_rows<LA, NT>(smem[0] + BN * kBK, ra, tid);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
-        if (more) {
-            load_rows<LW, NT>(rw, Wt, n0, N, K, (k0 + kt + 1) * kBK, tid);
-            load_rows<LA, NT>(ra, A, m0, Mp, K, (k0 + kt + 1) * kBK, tid);
-        }
-        const uint8_t* sw = smem[kt & 1];
-        const uint8_t* sa = smem[kt & 1] + BN * kBK;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c0 = kk * 4 + (lane >> 5) * 2;
-            v8i af[TN], bf[TM];
-#pragma unroll
-            for (int i = 0; i < TN; ++i) af[i] = frag(sw, wn * WTN + i * 32 + (lane & 31), c0);
-#pragma unroll
-            for (int j = 0; j < TM; ++j) bf[j] = frag(sa, wm * WTM + j * 32 + (lane & 31), c0);
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-#pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-        }
-        if (more) {
-            store_rows<LW, NT>(smem[(kt + 1) & 1], rw, tid);
-            store_rows<LA, NT>(smem[(kt + 1) & 1] + BN * kBK, ra, tid);
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: y = acc * (s_act * s_w), fp32 row-major
-    if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    const float s = act_scale[1] * w_scale;
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int m = m0 + wm * WTM + j * 32 + (lane & 31);
-            if (m >= M) continue;
-            float* yrow = Y + (size_t)m * N;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-                const float4 v = make_float4(acc[i][j][4 * g] * s, acc[i][j][4 * g + 1] * s,
-                                             acc[i][j][4 * g + 2] * s, acc[i][j][4 * g + 3] * s);
-                if (vec && n + 3 < N) {
-                    *reinterpret_cast<float4*>(yrow + n) = v;
-                } else {
-                    if (n < N) yrow[n] = v.x;
-                    if (n + 1 < N) yrow[n + 1] = v.y;
-                    if (n + 2 < N) yrow[n + 2] = v.z;
-                    if (n + 3 < N) yrow[n + 3] = v.w;
-                }
-            }
-        }
-    }
-}
-
-enum Kind { kTiles = 0, kMedium = 1, kSmall = 2, kLargeEdge = 3 };
-
 struct KindInfo {
     int bn, bm, threads;
 };
-constexpr KindInfo kKinds[4] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}, {256, 256, 256}};
+// indexed by GemmKind
+constexpr KindInfo kKinds[5] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}, {256, 256, 256}, {16, 0, 256}};
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-
-// Arrival counters of the split tiles (one uint32 each), padded to 256 bytes;
-// the partial sums follow.
-size_t split_counter_bytes(int rem) { return ((size_t)rem * sizeof(unsigned) + 255) / 256 * 256; }
 
 // K chunks per tile for the edge-capable kinds.  The 128x128 kernel (two
 // workgroups per CU) splits until the chunks fill one workgroup per CU, in
@@ -759,10 +338,10 @@ size_t split_counter_bytes(int rem) { return ((size_t)rem * sizeof(unsigned) + 2
 int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
     const int pairs = (int)(k / 256u);
     int s = 1;
-    if (kind == kMedium) {
+    if (kind == kGemmMedium) {
         const int T = ceil_div(mp, 128) * ceil_div((int)n, 128);
         s = 256 / T < pairs / 2 ? 256 / T : pairs / 2;
-    } else if (kind == kSmall) {
+    } else if (kind == kGemmSmall) {
         const int T = ceil_div(mp, 32) * ceil_div((int)n, 64);
         s = 512 / T < pairs ? 512 / T : pairs;
     }
@@ -772,6 +351,8 @@ int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
 }  // namespace
 
 // Kernel choice per shape:
+//  * the skinny kernel (16 weight rows per workgroup, K split over its
+//    waves) when padded M <= 64;
 //  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
 //    as half tiles when they fit one round) when N and padded M are
 //    multiples of 256, K >= 512, N <= 2^21 and there are at least 64 tiles;
@@ -787,7 +368,7 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     p.s = 1;
     const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
     if (mp % 256 == 0 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
-        p.kind = kTiles;
+        p.kind = kGemmTiles;
         p.G = cus;
         const int tiles_m = mp / 256;
         p.R = t256 / cus;
@@ -802,17 +383,21 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
             p.rem = 0;
             p.workgroups = t256;
         }
+    } else if (mp <= 64) {
+        p.kind = kGemmSkinny;
     } else if (t256 >= 256) {
-        p.kind = kLargeEdge;
-    } else if (mp >= 128 && ceil_div(mp, 128) * ceil_div((int)n, 128) * edge_split(kMedium, mp, n, k) >= 128) {
-        p.kind = kMedium;
+        p.kind = kGemmLargeEdge;
+    } else if (mp >= 128 && ceil_div(mp, 128) * ceil_div((int)n, 128) * edge_split(kGemmMedium, mp, n, k) >= 128) {
+        p.kind = kGemmMedium;
     } else {
-        p.kind = kSmall;
+        p.kind = kGemmSmall;
     }
     p.bn = kKinds[p.kind].bn;
-    p.bm = kKinds[p.kind].bm;
+    p.bm = p.kind == kGemmSkinny ? mp : kKinds[p.kind].bm;
     p.threads = kKinds[p.kind].threads;
-    if (p.kind != kTiles) {
+    if (p.kind == kGemmSkinny) {
+        p.workgroups = ceil_div((int)n, 16);
+    } else if (p.kind != kGemmTiles) {
         const int T = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
         p.workgroups = T;
         p.s = split_allowed ? edge_split(p.kind, mp, n, k) : 1;
@@ -831,46 +416,22 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     GemmPlan p = plan_gemm(m, n, k, cus, true);
     if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
         p = plan_gemm(m, n, k, cus, false);  // no room for partial sums: whole tiles only
-    const int mp = (int)((m + 15u) & ~15u);
-    const int tiles_m = ceil_div(mp, p.bm), tiles_n = ceil_div((int)n, p.bn);
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
-    SplitK S = {1, (int)(k / 256u), nullptr, nullptr};
-    if (p.kind != kTiles && p.s > 1) {
-        S.s = p.s;
-        S.cnt = static_cast<unsigned*>(ws);
-        S.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_counter_bytes(p.rem));
-    }
-    switch (p.kind) {
-        case kTiles: {
-            InteriorPlan ip;
-            ip.tiles_m = tiles_m;
-            ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
-            ip.nd = p.workgroups / tiles_m;
-            ip.group_m = group_m;
-            ip.nhalf = 2 * p.rem;
-            // groups of about sqrt(2 * halves per XCD) halves: each XCD's block
-            // of half tiles is near square in elements
-            const int per_xcd = ceil_div(ip.nhalf, kXcds);
-            int hgm = 1;
-            while (hgm * 2 <= 2 * tiles_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
-            ip.half_gm = hgm;
-            fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, (int)n, (int)k, act_scale, w_scale, ip);
-            break;
-        }
-        case kLargeEdge:
-            fp8_gemm_deep_kernel<256, 256, 2, 2, false><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
-            break;
-        case kMedium:
-            fp8_gemm_deep_kernel<128, 128, 2, 2, true><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
-            break;
-        default:
-            fp8_gemm_kernel<64, 32, 2, 1><<<p.workgroups, p.threads, 0, st>>>(
-                a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
-            break;
-    }
+    if (p.kind != kGemmTiles) return launch_gemm_edge(p, a_fp8, w_fp8, m, n, k, act_scale, w_scale, y, ws, st);
+    const int tiles_m = (int)(m + 15u) / 256;  // padded M is a multiple of 256 here
+    InteriorPlan ip;
+    ip.tiles_m = tiles_m;
+    ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
+    ip.nd = p.workgroups / tiles_m;
+    ip.group_m = tiles_m < 8 ? tiles_m : 8;
+    ip.nhalf = 2 * p.rem;
+    // groups of about sqrt(2 * halves per XCD) halves: each XCD's block of
+    // half tiles is near square in elements
+    const int per_xcd = ceil_div(ip.nhalf, kXcds);
+    int hgm = 1;
+    while (hgm * 2 <= 2 * tiles_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
+    ip.half_gm = hgm;
+    fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n,
+                                                                             (int)k, act_scale, w_scale, ip);
     return hipGetLastError();
 }
 

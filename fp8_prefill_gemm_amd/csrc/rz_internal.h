@@ -31,7 +31,8 @@ hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* o
                          hipStream_t st);
 hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hipStream_t st);
 
-// ---- gemm.hip
+// ---- gemm.hip, gemm_edge.hip
+enum GemmKind { kGemmTiles = 0, kGemmMedium = 1, kGemmSmall = 2, kGemmLargeEdge = 3, kGemmSkinny = 4 };
 struct GemmPlan {
     int bn, bm, threads, workgroups, kind;
     // interior-tile plan: CUs, whole-tile rounds, tiles left over (run as
@@ -45,5 +46,12 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
 hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                        uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
                        size_t ws_bytes, int cus, hipStream_t st);
+// The kernels of every plan kind but kGemmTiles (gemm_edge.hip); ws holds
+// the split-K counters and partial sums when p.s > 1.
+hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
+                            uint32_t k, const float* act_scale, float w_scale, float* y, void* ws, hipStream_t st);
+// Split-K workspace: arrival counters of the split tiles (one uint32 each),
+// padded to 256 bytes; the partial sums follow.
+inline size_t split_counter_bytes(int tiles) { return ((size_t)tiles * sizeof(unsigned) + 255) / 256 * 256; }
 
 }  // namespace rz

@@ -298,10 +298,35 @@ def test_gemm_interior_plans(rz, m, n, k, full):
         assert (err <= tol).all(), f"{(err > tol).sum()} out of bound"
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (1, 4608, 3584),     # one activation block, 288 workgroups, 7 K-steps per wave
+    (4, 200, 768),       # ragged last block of weight rows, 1-2 K-steps per wave
+    (37, 200, 2816),     # three activation blocks (M_pad 48)
+    (48, 4608, 3584),    # three full blocks
+    (64, 258, 256),      # four blocks, n % 4 != 0, waves without K-steps
+    (17, 1000, 18944),   # two blocks, 37 K-steps per wave in register chunks
+    (16, 256, 512),      # configuration 1 shape
+])
+def test_gemm_skinny(rz, m, n, k):
+    bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+    mp = fp8_path.pad_m(m)
+    assert (bn, bm, threads, wgs) == (16, mp, 256, -(-n // 16))
+    assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
+    g = np.random.Generator(np.random.PCG64(m * 5 + n + k))
+    a8 = _codes(g, (mp, k))
+    a8[m:] = 0
+    w8 = _codes(g, (n, k))
+    sc = np.array([1.0, 0.017, 0, 0], np.float32)
+    wdq = np.float32(0.0071)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), float(wdq)))
+    assert y.shape == (m, n)
+    check_gemm(y, a8, w8, m, sc[1], wdq)
+
+
 @pytest.mark.parametrize("m,n,k,full", [
-    (4, 200, 768, True),       # 64x32 tiles, 3 K chunks of 1 pair, ragged n
-    (37, 200, 2816, True),     # 64x32 tiles, 11 chunks, ragged m and n
-    (1, 4608, 3584, True),     # 64x32 tiles, 7 chunks of 2 pairs
+    (80, 200, 768, True),      # 64x32 tiles, 3 K chunks of 1 pair, ragged m and n
+    (65, 1000, 2816, True),    # 64x32 tiles, 10 uneven chunks
+    (96, 4608, 3584, False),   # 64x32 tiles, 2 chunks of 7 pairs
     (300, 520, 2048, True),    # 64x32 tiles, 5 uneven chunks
     (600, 1000, 3584, False),  # 128x128 tiles, 6 uneven chunks, ragged m and n
     (512, 3584, 3584, False),  # 128x128 tiles in 2 chunks
