@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
                   for f in ("gemm.hip", "gemm_common.h", "rz_internal.h")]
@@ -225,7 +226,21 @@ def main() -> int:
     gateup_us = 0.5 * (ph["gemm_gate"] + ph["gemm_up"])
     achieved = flop["gate"] / (gateup_us * 1e-6) / 1e12
     plan = rz.rz_fp8_gemm_plan(M, gate.n, gate.k)
+    # HBM-bound phases: algorithmic bytes (blocks read twice + 1 B per weight
+    # written; activations read twice as fp32 + 1 B per element written)
+    # against the 8 TB/s HBM peak
+    Mp_ffn = rz.rz_pad_m(M)
+    algo = {
+        "pack_gate": 2 * gate_blocks_h.nbytes + gate.n * gate.k,
+        "pack_up": 2 * up_blocks_h.nbytes + up.n * up.k,
+        "pack_down": 2 * down_blocks_h.nbytes + dn.n * dn.k,
+        "quant_ffn": 2 * x_ffn_h.nbytes + Mp_ffn * ffn.k,
+        "quant_down": 2 * x_down_h.nbytes + Mp_ffn * down.k,
+    }
+    hbm = {k: {"algorithmic_bytes": int(b), "tb_per_s": round(b / (ph[k] * 1e-6) / 1e12, 3),
+               "frac": round(b / (ph[k] * 1e-6) / 1e12 / HBM_PEAK_TBPS, 4)} for k, b in algo.items()}
     log("phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in ph.items()))
+    log("HBM-bound phases: " + " ".join(f"{k}={v['tb_per_s']:.2f}TB/s({v['frac']:.0%})" for k, v in hbm.items()))
     log(f"gate/up GEMM {gateup_us:.1f} us = {achieved:.1f} TFLOP/s ({achieved / FP8_PEAK_TFLOPS:.1%} of peak), "
         f"plan BNxBM={plan[0]}x{plan[1]} threads={plan[2]} wgs={plan[3]}")
 
@@ -257,6 +272,7 @@ def main() -> int:
             "traffic": measured_traffic(),
         },
         "phases_us": {k: round(v, 2) for k, v in ph.items()},
+        "hbm_phases": hbm,
         "gemm_tflops": {k: round(v, 2) for k, v in gemm_tflops.items()},
         "cpu_baseline": None,
     }

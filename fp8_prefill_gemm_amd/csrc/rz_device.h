@@ -215,6 +215,20 @@ __device__ __forceinline__ void q4k_decode_unit(uint4 head, uint4 qs, int s, Q4U
     }
 }
 
+// Running per-byte maximum and minimum of the four bytes of w (each < 256)
+// with packed 16-bit integer max/min: bytes 0 and 2 go to the two 16-bit
+// halves of one operand, bytes 1 and 3 to the other.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void byte_minmax(uint32_t w, u16x2& mx, u16x2& mn) {
+    const u16x2 e = __builtin_bit_cast(u16x2, w & 0x00FF00FFu);
+    const u16x2 o = __builtin_bit_cast(u16x2, (w >> 8) & 0x00FF00FFu);
+    mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(e, o));
+    mn = __builtin_elementwise_min(mn, __builtin_elementwise_min(e, o));
+}
+__device__ __forceinline__ uint32_t u16x2_max(u16x2 v) { return v.x > v.y ? v.x : v.y; }
+__device__ __forceinline__ uint32_t u16x2_min(u16x2 v) { return v.x < v.y ? v.x : v.y; }
+
 // max abs_key over the 32 decoded values of a unit, without decoding them:
 // d*sc*q is exact, so q -> RN(d*sc*q - dmin*m) is monotone in q and |value|
 // peaks at the smallest or the largest nibble of each half (NaN products
@@ -230,19 +244,15 @@ __device__ __forceinline__ uint32_t q4k_unit_key(uint4 head, uint4 qs, int s) {
     const float d0 = d * (float)sc0, o0 = dmin * (float)m0;
     const float d1 = d * (float)sc1, o1 = dmin * (float)m1;
     const uint32_t w[4] = {qs.x, qs.y, qs.z, qs.w};
-    float lmax = 0.0f, lmin = 15.0f, hmax = 0.0f, hmin = 15.0f;
+    u16x2 lmx = {0, 0}, lmn = {15, 15}, hmx = {0, 0}, hmn = {15, 15};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float ql = (float)((lo >> (8 * b)) & 0xFFu), qh = (float)((hi >> (8 * b)) & 0xFFu);
-            lmax = fmaxf(lmax, ql);
-            lmin = fminf(lmin, ql);
-            hmax = fmaxf(hmax, qh);
-            hmin = fminf(hmin, qh);
-        }
+        byte_minmax(lo, lmx, lmn);
+        byte_minmax(hi, hmx, hmn);
     }
+    const float lmax = (float)u16x2_max(lmx), lmin = (float)u16x2_min(lmn);
+    const float hmax = (float)u16x2_max(hmx), hmin = (float)u16x2_min(hmn);
     const uint32_t k0 = abs_key(d0 * lmax - o0), k1 = abs_key(d0 * lmin - o0);
     const uint32_t k2 = abs_key(d1 * hmax - o1), k3 = abs_key(d1 * hmin - o1);
     const uint32_t a = k0 > k1 ? k0 : k1, b = k2 > k3 ? k2 : k3;
@@ -291,22 +301,24 @@ __device__ __forceinline__ uint32_t q6k_unit_key(uint4 ql_a, uint4 ql_b, uint4 q
     const uint32_t A[4] = {ql_a.x, ql_a.y, ql_a.z, ql_a.w};
     const uint32_t B[4] = {ql_b.x, ql_b.y, ql_b.z, ql_b.w};
     const uint32_t H[4] = {qh.x, qh.y, qh.z, qh.w};
-    float qmax[4] = {0.0f, 0.0f, 0.0f, 0.0f}, qmin[4] = {63.0f, 63.0f, 63.0f, 63.0f};
+    u16x2 mx[4], mn[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        mx[p] = (u16x2){0, 0};
+        mn[p] = (u16x2){63, 63};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t q[4];
-        q[0] = (A[i] & 0x0F0F0F0Fu) | ((H[i] & 0x03030303u) << 4);
-        q[1] = (B[i] & 0x0F0F0F0Fu) | (((H[i] >> 2) & 0x03030303u) << 4);
-        q[2] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 4) & 0x03030303u) << 4);
-        q[3] = ((B[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 6) & 0x03030303u) << 4);
+        byte_minmax((A[i] & 0x0F0F0F0Fu) | ((H[i] & 0x03030303u) << 4), mx[0], mn[0]);
+        byte_minmax((B[i] & 0x0F0F0F0Fu) | (((H[i] >> 2) & 0x03030303u) << 4), mx[1], mn[1]);
+        byte_minmax(((A[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 4) & 0x03030303u) << 4), mx[2], mn[2]);
+        byte_minmax(((B[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> 6) & 0x03030303u) << 4), mx[3], mn[3]);
+    }
+    float qmax[4], qmin[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float f = (float)((q[p] >> (8 * b)) & 0xFFu);
-                qmax[p] = fmaxf(qmax[p], f);
-                qmin[p] = fminf(qmin[p], f);
-            }
+    for (int p = 0; p < 4; ++p) {
+        qmax[p] = (float)u16x2_max(mx[p]);
+        qmin[p] = (float)u16x2_min(mn[p]);
     }
     uint32_t key = 0;
 #pragma unroll
