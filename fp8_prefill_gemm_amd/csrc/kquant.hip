@@ -179,13 +179,14 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
         visit_units<14>(blocks, nb, lds,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             Q6Unit u;
-                            q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
                             uint8_t* o = w_fp8 + b * kQK + 128 * h + l0;
                             if (__all(tensor_finite && half_finite(dbits))) {
+                                q6k_decode_unit<true>(ql_a, ql_b, qh, sc4, dbits, u);
 #pragma unroll
                                 for (int p = 0; p < 4; ++p)
                                     *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16<true>(u.v[p], q);
                             } else {
+                                q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
 #pragma unroll
                                 for (int p = 0; p < 4; ++p)
                                     *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16(u.v[p], q);

@@ -207,10 +207,13 @@ __device__ __forceinline__ void q4k_decode_unit(uint4 head, uint4 qs, int s, Q4U
         // byte-to-float conversion per value)
         uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
         asm("" : "+v"(lo), "+v"(hi));  // keep the masks: byte b converts with v_cvt_f32_ubyte<b>
+        // d0*q is exact (an 11-bit f16 significand times a 6-bit scale times a
+        // 4-bit quant), so the fused multiply-add rounds exactly once, as
+        // the multiply and the subtraction do
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            u.lo[4 * i + b] = d0 * (float)((lo >> (8 * b)) & 0xFFu) - o0;
-            u.hi[4 * i + b] = d1 * (float)((hi >> (8 * b)) & 0xFFu) - o1;
+            u.lo[4 * i + b] = __builtin_fmaf(d0, (float)((lo >> (8 * b)) & 0xFFu), -o0);
+            u.hi[4 * i + b] = __builtin_fmaf(d1, (float)((hi >> (8 * b)) & 0xFFu), -o1);
         }
     }
 }
@@ -268,6 +271,10 @@ struct Q6Unit {
     float v[4][16];
 };
 
+// kFinite: the caller knows d is finite, so ds*(q-32), which is exact, can
+// be computed as ds*q - 32*ds in one fused multiply-add (with an infinite d
+// that form would give NaN where the product gives an infinity).
+template <bool kFinite = false>
 __device__ __forceinline__ void q6k_decode_unit(uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4,
                                                 uint32_t dbits, Q6Unit& u) {
     const float d = half_bits_to_float(dbits);
@@ -289,7 +296,10 @@ __device__ __forceinline__ void q6k_decode_unit(uint4 ql_a, uint4 ql_b, uint4 qh
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) u.v[p][4 * i + b] = ds[p] * ((float)((q[p] >> (8 * b)) & 0xFFu) - 32.0f);
+            for (int b = 0; b < 4; ++b) {
+                const float qf = (float)((q[p] >> (8 * b)) & 0xFFu);
+                u.v[p][4 * i + b] = kFinite ? __builtin_fmaf(ds[p], qf, -32.0f * ds[p]) : ds[p] * (qf - 32.0f);
+            }
     }
 }
 
