@@ -325,7 +325,7 @@ struct KindInfo {
     int bn, bm, threads;
 };
 // indexed by GemmKind
-constexpr KindInfo kKinds[5] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}, {256, 256, 256}, {16, 0, 256}};
+constexpr KindInfo kKinds[6] = {{256, 256, 256}, {128, 128, 256}, {64, 32, 128}, {256, 256, 256}, {16, 0, 256}, {4, 0, 256}};
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -351,6 +351,9 @@ int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
 }  // namespace
 
 // Kernel choice per shape:
+//  * the GEMV kernel (one weight row per wave, vector ALU) when M <= 3
+//    (measured: faster than the skinny kernel up to M = 2, equal at 3; the
+//    pages also route M < 4 to their GEMV path);
 //  * the skinny kernel (16 weight rows per workgroup, K split over its
 //    waves) when padded M <= 64;
 //  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
@@ -383,6 +386,8 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
             p.rem = 0;
             p.workgroups = t256;
         }
+    } else if (m <= 3) {
+        p.kind = kGemmGemv;
     } else if (mp <= 64) {
         p.kind = kGemmSkinny;
     } else if (t256 >= 256) {
@@ -393,9 +398,11 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
         p.kind = kGemmSmall;
     }
     p.bn = kKinds[p.kind].bn;
-    p.bm = p.kind == kGemmSkinny ? mp : kKinds[p.kind].bm;
+    p.bm = (p.kind == kGemmSkinny || p.kind == kGemmGemv) ? mp : kKinds[p.kind].bm;
     p.threads = kKinds[p.kind].threads;
-    if (p.kind == kGemmSkinny) {
+    if (p.kind == kGemmGemv) {
+        p.workgroups = ceil_div((int)n, 4);  // one weight row per wave
+    } else if (p.kind == kGemmSkinny) {
         p.workgroups = ceil_div((int)n, 16);
     } else if (p.kind != kGemmTiles) {
         const int T = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);

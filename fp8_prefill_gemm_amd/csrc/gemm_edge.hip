@@ -6,7 +6,8 @@
 //     with a two-deep register prefetch, optionally split along K;
 //   * fp8_gemm_kernel: 64x32 tiles with a one-deep prefetch, optionally
 //     split along K;
-//   * fp8_gemm_skinny_kernel: padded M <= 64, bound by the weight read.
+//   * fp8_gemm_skinny_kernel: padded M <= 64, bound by the weight read;
+//   * fp8_gemv_kernel: M <= 3, on the vector ALU.
 //
 // The tiled kernels walk K in steps of 128 bytes with two LDS stages: the
 // next step's global loads are issued before the current step's MFMAs and
@@ -561,6 +562,77 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void fp8_gemm_skinny_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// GEMV kernel: at most 3 real activation rows.  The MFMA tiles would be
+// mostly padding rows here, so the products run on the vector ALU: one
+// wave per weight row, lane l taking K bytes 1024c + 16l (c = 0, 1, ...) of
+// the row and of each activation row, with coalesced 16-byte loads (a wave
+// reads 1 KB of a row per load).  The bytes are decoded with
+// v_cvt_pk_f32_fp8 (OCP E4M3FN, as the encoder writes them); the product of
+// two decoded values is exact in fp32, and each lane accumulates its
+// products in K order with fused multiply-adds.  The 64 lane sums are added
+// by a butterfly over the wave and lane 0 stores y[m][n] for m < M.
+// ---------------------------------------------------------------------------
+typedef float v2f __attribute__((ext_vector_type(2)));
+constexpr int kGemvPass = 4;  // 1 KB chunks of K loaded per pass
+
+template <int MR>
+__device__ __forceinline__ void gemv_fma16(float (&acc)[MR], const u32x4& w, const u32x4 (&a)[MR]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const v2f w0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
+        const v2f w1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a[m][d], false);
+            const v2f a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a[m][d], true);
+            acc[m] = __builtin_fmaf(w0.x, a0.x, acc[m]);
+            acc[m] = __builtin_fmaf(w0.y, a0.y, acc[m]);
+            acc[m] = __builtin_fmaf(w1.x, a1.x, acc[m]);
+            acc[m] = __builtin_fmaf(w1.y, a1.y, acc[m]);
+        }
+    }
+}
+
+template <int MR>
+__global__ __launch_bounds__(256) void fp8_gemv_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt,
+                                                       float* __restrict__ Y, int N, int K,
+                                                       const float* __restrict__ act_scale, float w_scale) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);  // one weight row per wave
+    if (n >= N) return;                                // whole waves
+    const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(Wt + (size_t)n * K, (uint32_t)K);
+    __amdgpu_buffer_rsrc_t ars[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) ars[m] = tile_rsrc(A + (size_t)m * K, (uint32_t)K);
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+    // offsets at or past K fall outside the resources and read zero
+    for (int kb = 0; kb < K; kb += 1024 * kGemvPass) {
+        u32x4 w[kGemvPass], a[kGemvPass][MR];
+#pragma unroll
+        for (int c = 0; c < kGemvPass; ++c) {
+            const uint32_t off = (uint32_t)(kb + 1024 * c + 16 * lane);
+            w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                a[c][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars[m], off, 0, 0));
+        }
+#pragma unroll
+        for (int c = 0; c < kGemvPass; ++c) gemv_fma16<MR>(acc, w[c], a[c]);
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1) acc[m] += __shfl_xor(acc[m], sh, 64);
+    if (lane == 0) {
+        const float sc = act_scale[1] * w_scale;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) Y[(size_t)m * N + n] = acc[m] * sc;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
@@ -582,6 +654,13 @@ hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8
         case kGemmMedium:
             fp8_gemm_deep_kernel<128, 128, 2, 2, true><<<p.workgroups, p.threads, 0, st>>>(
                 a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
+            break;
+        case kGemmGemv:
+            switch (m) {
+                case 1: fp8_gemv_kernel<1><<<p.workgroups, p.threads, 0, st>>>(a_fp8, w_fp8, y, (int)n, (int)k, act_scale, w_scale); break;
+                case 2: fp8_gemv_kernel<2><<<p.workgroups, p.threads, 0, st>>>(a_fp8, w_fp8, y, (int)n, (int)k, act_scale, w_scale); break;
+                default: fp8_gemv_kernel<3><<<p.workgroups, p.threads, 0, st>>>(a_fp8, w_fp8, y, (int)n, (int)k, act_scale, w_scale); break;
+            }
             break;
         case kGemmSkinny:
             switch (mp / 16) {

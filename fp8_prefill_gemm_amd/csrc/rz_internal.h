@@ -32,7 +32,7 @@ hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* o
 hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hipStream_t st);
 
 // ---- gemm.hip, gemm_edge.hip
-enum GemmKind { kGemmTiles = 0, kGemmMedium = 1, kGemmSmall = 2, kGemmLargeEdge = 3, kGemmSkinny = 4 };
+enum GemmKind { kGemmTiles = 0, kGemmMedium = 1, kGemmSmall = 2, kGemmLargeEdge = 3, kGemmSkinny = 4, kGemmGemv = 5 };
 struct GemmPlan {
     int bn, bm, threads, workgroups, kind;
     // interior-tile plan: CUs, whole-tile rounds, tiles left over (run as

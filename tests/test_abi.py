@@ -115,7 +115,7 @@ def test_gemm_validation(L):
 
 
 def test_gemm_workspace_sizes(L):
-    # the skinny kernel (padded M <= 64) needs none; split-K with 64x32 tiles:
+    # the GEMV and skinny kernels (padded M <= 64) need none; split-K with 64x32 tiles:
     # 256 bytes of arrival counters + 12 tiles x 2 chunks of 64x32 fp32
     assert L.rz_fp8_gemm_workspace_bytes(16, 256, 512) == 0
     assert L.rz_fp8_gemm_workspace_bytes(80, 256, 512) == 256 + 12 * 2 * 64 * 32 * 4
@@ -164,13 +164,15 @@ def test_plans_cover_shapes(L):
 
 def _edge_plan(m, n, k, cus=256):
     """(BN, BM, workgroups, workspace bytes) of a plan that is not interior
-    (256 CUs): the skinny kernel (16 weight rows per workgroup) when M_pad <=
-    64; 256x256 tiles from 256 tiles on, unsplit; else 128x128 tiles
+    (256 CUs): the GEMV kernel (4 weight rows per workgroup) when M <= 3;
+    the skinny kernel (16 weight rows per workgroup) when M_pad <= 64; 256x256 tiles from 256 tiles on, unsplit; else 128x128 tiles
     split into s = min(256 // tiles, pairs // 2) K chunks if M_pad >= 128 and
     that gives >= 128 workgroups; else 64x32 tiles in s = min(512 // tiles,
     pairs) chunks.  A split rounds the tiles up to a multiple of 8 (XCDs)."""
     mp = -(-m // 16) * 16
     pairs = k // 256
+    if m <= 3:
+        return 4, mp, -(-n // 4), 0
     if mp <= 64:
         return 16, mp, -(-n // 16), 0
 

@@ -299,8 +299,29 @@ def test_gemm_interior_plans(rz, m, n, k, full):
 
 
 @pytest.mark.parametrize("m,n,k", [
-    (1, 4608, 3584),     # one activation block, 288 workgroups, 7 K-steps per wave
-    (4, 200, 768),       # ragged last block of weight rows, 1-2 K-steps per wave
+    (1, 4608, 3584),     # one row per wave, last 1 KB chunk of K half used
+    (3, 200, 768),       # three activation rows, K shorter than one pass
+    (3, 1000, 18944),    # five passes over K
+    (2, 17, 256),        # last workgroup with one row; lanes past K read zero
+])
+def test_gemm_gemv(rz, m, n, k):
+    bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+    assert (bn, bm, threads, wgs) == (4, 16, 256, -(-n // 4))
+    assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
+    g = np.random.Generator(np.random.PCG64(m * 11 + n + k))
+    a8 = _codes(g, (16, k))
+    a8[m:] = 0
+    w8 = _codes(g, (n, k))
+    sc = np.array([1.0, 0.019, 0, 0], np.float32)
+    wdq = np.float32(0.0083)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), float(wdq)))
+    assert y.shape == (m, n)
+    check_gemm(y, a8, w8, m, sc[1], wdq)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (4, 4608, 3584),     # one activation block, 288 workgroups, 7 K-steps per wave
+    (16, 200, 768),      # ragged last block of weight rows, 1-2 K-steps per wave
     (37, 200, 2816),     # three activation blocks (M_pad 48)
     (48, 4608, 3584),    # three full blocks
     (64, 258, 256),      # four blocks, n % 4 != 0, waves without K-steps
