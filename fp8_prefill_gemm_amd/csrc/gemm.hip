@@ -14,10 +14,14 @@
 // (v_mfma_f32_32x32x64_f8f6f4, E4M3 x E4M3 -> fp32, unscaled form).  Both
 // operands are K-contiguous, which is the native MFMA operand layout: lane l
 // of a 32x32x64 MFMA supplies row l%32 and 32 consecutive K bytes at offset
-// 32*(l/32), so no transpose is needed.  The weight is the MFMA "A" side
-// (output rows = n) and the activation the "B" side (columns = m), so each
-// lane ends with runs of 4 consecutive n of one output row m: 16-byte stores
-// into the row-major fp32 output.
+// 32*(l/32), so no transpose is needed.  In the interior kernel the
+// activation is the MFMA "A" side (result rows = m) and the weight the "B"
+// side (result columns = n): lane l then holds output column n = l%32 of
+// its block, so a store instruction writes two full 128-byte output row
+// segments (lanes 0-31 one row, 32-63 another).  With the roles the other
+// way round each lane holds 4 consecutive n and an instruction covers 32
+// rows x 32 bytes, which measured 2-7 % slower per launch on the large
+// shapes (same results: the products and their order are the same).
 //
 // This file: the 256x256 interior-tile kernel (the large prefill GEMMs),
 // the plan that picks a kernel per shape, and the launcher.  Kernels for
@@ -119,7 +123,7 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[g & 1], acc[i][j], 0, 0, 0,
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[g & 1], a[kk][i], acc[i][j], 0, 0, 0,
                                                                         0, 0, 0);
 #pragma unroll
         for (int c = kPer * g; c < kPer * g + kPer; ++c) {
@@ -167,15 +171,17 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
 // ---------------------------------------------------------------------------
 // Interior 256x256 tiles.
 //
-// When padded M and N are multiples of 256 the output splits into T whole
-// tiles.  G = one workgroup per CU; the first R*G tiles (R = floor(T/G) full
-// rounds, chosen as whole n-columns of tiles) run one tile per workgroup.
-// The rem = T - R*G tiles left over would leave most CUs idle for a whole
-// tile time; when 2*rem <= G each of them is cut into two half tiles of 128
-// activation rows that run on two CUs, as workgroups after the whole tiles
-// in the same launch, so the last round takes about half a tile time.  A
-// half tile runs the whole K range and stores its own output: no partial
-// sums, no workspace, no workgroup waits for another.
+// When N is a multiple of 256 the output splits into T = tiles_m * tiles_n
+// tiles of 256 x 256 (tiles_m = ceil(padded M / 256); see the kernel for a
+// padded M that is not a multiple of 256).  G = one workgroup per CU; the
+// first R*G tiles (R = floor(T/G) full rounds, chosen as whole n-columns of
+// tiles) run one tile per workgroup.  The rem = T - R*G tiles left over
+// would leave most CUs idle for a whole tile time; when their n-columns cut
+// into half tiles of 128 activation rows (ceil(padded M / 128) per column)
+// fit one round, those run as workgroups after the whole tiles in the same
+// launch, so the last round takes about half a tile time.  A half tile runs
+// the whole K range and stores its own output: no partial sums, no
+// workspace, no workgroup waits for another.
 //
 // The K loop (tile_mainloop): two LDS slots, the global loads three K-steps
 // ahead of the MFMAs in two register sets.
@@ -230,24 +236,27 @@ __device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][TM], uint8_t (&smem
     }
 }
 
-// acc * scale -> the 256 x 64*TM output tile at (n0, m0), float4 runs of an
-// output row.  `rs` covers the valid rows from m0 only, so the stores of
-// rows m >= M fall outside the buffer range and are dropped by the hardware
-// (no branches).
+// acc * scale -> the 256 x 64*TM output tile at (n0, m0).  acc[i][j][e]
+// is activation row wm*32*TM + 32j + 8*(e/4) + 4*(lane/32) + e%4 and
+// output column n0 + wn*128 + 32i + lane%32 (32x32 MFMA result layout with
+// the activation as the A operand), so each dword store covers 128
+// consecutive bytes of two output rows.  `rs` covers the valid rows from m0
+// only, so the stores of rows m >= M fall outside the buffer range and are
+// dropped by the hardware (no branches).
 template <int TM>
 __device__ __forceinline__ void store_acc(const v16f (&acc)[4][TM], __amdgpu_buffer_rsrc_t rs, uint32_t N,
                                           uint32_t n0, int wn, int wm, int lane, float scale) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < TM; ++j) {
+        const uint32_t row0 = (uint32_t)(wm * 32 * TM + j * 32 + 4 * (lane >> 5));
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const uint32_t row = (uint32_t)(wm * 32 * TM + j * 32 + (lane & 31));
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t col = n0 + (uint32_t)(wn * 128 + i * 32 + (lane & 31));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t col = n0 + (uint32_t)(wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5));
-                const float4 v = make_float4(acc[i][j][4 * q] * scale, acc[i][j][4 * q + 1] * scale,
-                                             acc[i][j][4 * q + 2] * scale, acc[i][j][4 * q + 3] * scale);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (row * N + col) * 4u, 0, 0);
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t row = row0 + (uint32_t)(8 * (e >> 2) + (e & 3));
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[i][j][e] * scale), rs,
+                                                      (row * N + col) * 4u, 0, 0);
             }
         }
     }
@@ -266,12 +275,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
 //   XCD w % 8, so XCD x is given the contiguous range [x*T/8, (x+1)*T/8) of
 //   that order: the workgroups that run together on one XCD share weight
 //   and activation rows through its L2.
-//   Half tiles: n-columns [nd, tiles_n) by 2*tiles_m activation halves of
+//   Half tiles: n-columns [nd, tiles_n) by halves_m activation halves of
 //   128 rows, nhalf of them in a grouped order with groups of half_gm
 //   halves; XCD x again takes a contiguous range of that order.
+// When the padded M (mp, a multiple of 16) is not a multiple of the tile
+// height, the last m-tile (half) starts at mp - 256 (mp - 128) instead: it
+// overlaps the one before it, so every row it loads exists, and the rows
+// both compute get the same operands in the same order, so both store the
+// same values there.
 struct InteriorPlan {
     int tiles_m, nd, nwhole, group_m;
-    int nhalf, half_gm;
+    int halves_m, nhalf, half_gm;
 };
 
 // Contiguous share of XCD x (workgroup w) of T items in order; false if w
@@ -299,10 +313,12 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
     const uint32_t step = 32u * (uint32_t)K;
     const float scale = act_scale[1] * w_scale;
+    const int mp = (M + 15) & ~15;  // >= 256 here
     int t, n0, m0;
     if (bid < P.nwhole) {
         (void)xcd_item(bid, P.nwhole, t);
         grouped_origin_bb<256, 256>(t, P.tiles_m, P.nd, P.group_m, n0, m0);
+        m0 = m0 < mp - 256 ? m0 : mp - 256;
         const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
         v16f acc[4][4];
         tile_mainloop<4>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
@@ -312,7 +328,8 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     }
     // nwhole is a multiple of 8: the half tiles' workgroups keep w % 8
     if (!xcd_item(bid - P.nwhole, P.nhalf, t)) return;
-    grouped_origin_bb<256, 128>(t, 2 * P.tiles_m, (N >> 8) - P.nd, P.half_gm, n0, m0);
+    grouped_origin_bb<256, 128>(t, P.halves_m, (N >> 8) - P.nd, P.half_gm, n0, m0);
+    m0 = m0 < mp - 128 ? m0 : mp - 128;
     n0 += P.nd * 256;
     const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
     v16f acc[4][2];
@@ -357,8 +374,8 @@ int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
 //  * the skinny kernel (16 weight rows per workgroup, K split over its
 //    waves) when padded M <= 64;
 //  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
-//    as half tiles when they fit one round) when N and padded M are
-//    multiples of 256, K >= 512, N <= 2^21 and there are at least 64 tiles;
+//    as half tiles when they fit one round) when N is a multiple of 256,
+//    padded M >= 256, K >= 512, N <= 2^21 and there are at least 64 tiles;
 //  * 256x256 edge-capable kernel when tiles cross N or padded M but there are
 //    still >= 256 of them;
 //  * 128x128 tiles when M_pad >= 128 and tiles times K chunks give >= 128
@@ -370,17 +387,18 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     GemmPlan p = {};
     p.s = 1;
     const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
-    if (mp % 256 == 0 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
+    if (mp >= 256 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
         p.kind = kGemmTiles;
         p.G = cus;
-        const int tiles_m = mp / 256;
+        const int tiles_m = ceil_div(mp, 256);
         p.R = t256 / cus;
         // the whole-tile rounds must be whole n-columns of tiles
         if ((p.R * cus) % tiles_m != 0) p.R = 0;
         p.rem = t256 - p.R * cus;
-        if (p.rem > 0 && 2 * p.rem <= cus) {  // last round in half tiles
+        const int nhalf = ceil_div(mp, 128) * (p.rem / tiles_m);  // halves of the leftover n-columns
+        if (p.rem > 0 && nhalf <= cus) {  // last round in half tiles
             p.workgroups = p.R * cus;
-            p.half_workgroups = kXcds * ceil_div(2 * p.rem, kXcds);
+            p.half_workgroups = kXcds * ceil_div(nhalf, kXcds);
         } else {  // every tile whole
             p.R = t256 / cus;
             p.rem = 0;
@@ -424,18 +442,20 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
         p = plan_gemm(m, n, k, cus, false);  // no room for partial sums: whole tiles only
     if (p.kind != kGemmTiles) return launch_gemm_edge(p, a_fp8, w_fp8, m, n, k, act_scale, w_scale, y, ws, st);
-    const int tiles_m = (int)(m + 15u) / 256;  // padded M is a multiple of 256 here
+    const int mp = (int)((m + 15u) & ~15u);
+    const int tiles_m = ceil_div(mp, 256);
     InteriorPlan ip;
     ip.tiles_m = tiles_m;
     ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
     ip.nd = p.workgroups / tiles_m;
     ip.group_m = tiles_m < 8 ? tiles_m : 8;
-    ip.nhalf = 2 * p.rem;
+    ip.halves_m = ceil_div(mp, 128);
+    ip.nhalf = ip.halves_m * (p.rem / tiles_m);
     // groups of about sqrt(2 * halves per XCD) halves: each XCD's block of
     // half tiles is near square in elements
     const int per_xcd = ceil_div(ip.nhalf, kXcds);
     int hgm = 1;
-    while (hgm * 2 <= 2 * tiles_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
+    while (hgm * 2 <= ip.halves_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
     ip.half_gm = hgm;
     fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n,
                                                                              (int)k, act_scale, w_scale, ip);

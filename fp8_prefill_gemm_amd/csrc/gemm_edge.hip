@@ -103,7 +103,7 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* st
             const v8i bf = frag(sa, wm * WTM + j * 32 + (lane & 31), c0);
 #pragma unroll
             for (int i = 0; i < TN; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf, acc[i][j], 0, 0,
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af[i], acc[i][j], 0, 0,
                                                                             0, 0, 0, 0);
         }
     }
@@ -198,6 +198,29 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& 
     return true;
 }
 
+// acc * scale -> Y for a TN x TM wave tile whose rows start at m0 and
+// columns at n0.  With the activation as the MFMA A operand, acc[i][j][e]
+// is row m0 + 32j + 8*(e/4) + 4*(lane/32) + e%4, column n0 + 32i + lane%32:
+// a store instruction covers two 128-byte row segments.  Elements outside
+// [0, M) x [0, N) are skipped.
+template <int TN, int TM, int WTN, int WTM>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[TN][TM], float* __restrict__ Y, int M, int N, int m0,
+                                           int n0, int lane, float s) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const int n = n0 + i * 32 + (lane & 31);
+        if (n >= N) continue;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m < M) Y[(size_t)m * N + n] = acc[i][j][e] * s;
+            }
+        }
+    }
+}
+
 template <int BN, int BM, int WN, int WM, bool kSplit>
 __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
@@ -275,31 +298,7 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
 
     if constexpr (kSplit)  // (the 256x256 instance never splits: its registers are full)
         if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    const float s = act_scale[1] * w_scale;
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int m = m0 + wm * WTM + j * 32 + (lane & 31);
-            if (m >= M) continue;
-            float* yrow = Y + (size_t)m * N;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-                const float4 v = make_float4(acc[i][j][4 * g] * s, acc[i][j][4 * g + 1] * s,
-                                             acc[i][j][4 * g + 2] * s, acc[i][j][4 * g + 3] * s);
-                if (vec && n + 3 < N) {
-                    *reinterpret_cast<float4*>(yrow + n) = v;
-                } else {
-                    if (n < N) yrow[n] = v.x;
-                    if (n + 1 < N) yrow[n + 1] = v.y;
-                    if (n + 2 < N) yrow[n + 2] = v.z;
-                    if (n + 3 < N) yrow[n + 3] = v.w;
-                }
-            }
-        }
-    }
+    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane, act_scale[1] * w_scale);
 }
 
 template <int BN, int BM, int WN, int WM>
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
 #pragma unroll
                 for (int j = 0; j < TM; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                        bf[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
         }
         if (more) {
             store_rows<LW, NT>(smem[(kt + 1) & 1], rw, tid);
@@ -378,31 +377,7 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
 
     // ---- epilogue: y = acc * (s_act * s_w), fp32 row-major
     if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    const float s = act_scale[1] * w_scale;
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int m = m0 + wm * WTM + j * 32 + (lane & 31);
-            if (m >= M) continue;
-            float* yrow = Y + (size_t)m * N;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-                const float4 v = make_float4(acc[i][j][4 * g] * s, acc[i][j][4 * g + 1] * s,
-                                             acc[i][j][4 * g + 2] * s, acc[i][j][4 * g + 3] * s);
-                if (vec && n + 3 < N) {
-                    *reinterpret_cast<float4*>(yrow + n) = v;
-                } else {
-                    if (n < N) yrow[n] = v.x;
-                    if (n + 1 < N) yrow[n + 1] = v.y;
-                    if (n + 2 < N) yrow[n + 2] = v.z;
-                    if (n + 3 < N) yrow[n + 3] = v.w;
-                }
-            }
-        }
-    }
+    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane, act_scale[1] * w_scale);
 }
 
 // ---------------------------------------------------------------------------

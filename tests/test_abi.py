@@ -153,9 +153,9 @@ def test_plans_cover_shapes(L):
         bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
         mp = rz.rz_pad_m(m)
         tiles = -(-mp // bm) * -(-n // bn)
-        interior = (bn, bm) == (256, 256) and mp % 256 == 0 and n % 256 == 0 and k >= 512 and tiles >= 64
+        interior = (bn, bm) == (256, 256) and mp >= 256 and n % 256 == 0 and k >= 512 and tiles >= 64
         if interior:
-            assert wgs == _interior_wgs(mp // 256, n // 256, k)
+            assert wgs == _interior_wgs(mp, n // 256, k)
         else:
             assert (bn, bm, wgs) == _edge_plan(m, n, k)[:3]
             assert wgs >= tiles
@@ -194,18 +194,21 @@ def _edge_plan(m, n, k, cus=256):
     return bn, bm, 8 * -(-t // 8) * s, -(-4 * t // 256) * 256 + t * s * bn * bm * 4
 
 
-def _interior_wgs(tiles_m, tiles_n, k, cus=256):
-    """Workgroups of an interior-tile plan (256 CUs without a device): whole
-    tiles for the full rounds (whole n-columns of tiles, else none), then the
-    leftover tiles as two half tiles each when they fit one round (rounded up
-    to a multiple of 8 XCDs), or every tile whole."""
+def _interior_wgs(mp, tiles_n, k, cus=256):
+    """Workgroups of an interior-tile plan (256 CUs without a device) for a
+    padded M of mp rows: whole 256x256 tiles (ceil(mp/256) per n-column) for
+    the full rounds (whole n-columns of tiles, else none), then the leftover
+    n-columns as half tiles of 128 rows (ceil(mp/128) per column) when those
+    fit one round (rounded up to a multiple of 8 XCDs), or every tile whole."""
+    tiles_m = -(-mp // 256)
     t = tiles_m * tiles_n
     r = t // cus
     if (r * cus) % tiles_m:
         r = 0
     rem = t - r * cus
-    if 0 < rem and 2 * rem <= cus:
-        return r * cus + 8 * -(-2 * rem // 8)
+    nhalf = -(-mp // 128) * (rem // tiles_m)
+    if 0 < rem and nhalf <= cus:
+        return r * cus + 8 * -(-nhalf // 8)
     return t
 
 

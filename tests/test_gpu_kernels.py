@@ -275,13 +275,20 @@ def _codes(g, shape):
     (4096, 4608, 1024, False),   # 288 tiles: one round + 32 tiles as halves
     (768, 25600, 512, False),    # 300 tiles, rounds not whole n-columns: all whole
     (2040, 3584, 4864, False),   # 112 tiles as half tiles with long K, rows >= M dropped
+    # padded M not a multiple of 256: the last m-tile (half) is moved up to
+    # end at the last activation row and overlaps the one before it
+    (2000, 18944, 512, False),   # 2 rounds + 10 n-columns of 16 halves; last tile at 1744, half at 1872
+    (1900, 2560, 1024, True),    # halves only, 15 per n-column (the last at 1776)
+    (300, 16384, 512, False),    # 3 halves per n-column: 0, 128 and 176
+    (600, 25600, 512, False),    # 300 whole tiles, the last m-tile at 352
+    (1000, 65536, 512, False),   # 4 whole rounds, the last m-tile at 752
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
     from tests.test_abi import _interior_wgs
     mp = fp8_path.pad_m(m)
     bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
     assert (bn, bm, threads) == (256, 256, 256)
-    assert wgs == _interior_wgs(mp // 256, n // 256, k)
+    assert wgs == _interior_wgs(mp, n // 256, k)
     assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
     g = np.random.Generator(np.random.PCG64(m + n + k))
     a8, w8 = _codes(g, (mp, k)), _codes(g, (n, k))
@@ -289,7 +296,9 @@ def test_gemm_interior_plans(rz, m, n, k, full):
     sc = np.array([1.0, 0.03, 0, 0], np.float32)
     wdq = np.float32(0.011)
     A, Wd, S = dev(a8), dev(w8), dev(sc)
-    rows = np.arange(m) if full else np.unique(np.concatenate([[0, 1, m - 1], g.choice(m, 61, replace=False)]))
+    # sampled rows include a band over the last 300 rows (overlapping tiles)
+    rows = np.arange(m) if full else np.unique(np.concatenate(
+        [[0, 1, m - 1], g.choice(m, 61, replace=False), np.arange(max(0, m - 300), m, 7)]))
     yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
     for _ in range(2):  # twice in a row: nothing carried over between calls
         y = host(rz.rz_fp8_gemm(A, Wd, m, S, float(wdq)))
