@@ -171,9 +171,9 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
 // ---------------------------------------------------------------------------
 // Interior 256x256 tiles.
 //
-// When N is a multiple of 256 the output splits into T = tiles_m * tiles_n
-// tiles of 256 x 256 (tiles_m = ceil(padded M / 256); see the kernel for a
-// padded M that is not a multiple of 256).  G = one workgroup per CU; the
+// The output splits into T = tiles_m * tiles_n tiles of 256 x 256
+// (tiles_m = ceil(padded M / 256), tiles_n = ceil(N / 256); see the kernel
+// for the last tile when padded M or N is not a multiple of 256).  G = one workgroup per CU; the
 // first R*G tiles (R = floor(T/G) full rounds, chosen as whole n-columns of
 // tiles) run one tile per workgroup.  The rem = T - R*G tiles left over
 // would leave most CUs idle for a whole tile time; when their n-columns cut
@@ -279,12 +279,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
 //   128 rows, nhalf of them in a grouped order with groups of half_gm
 //   halves; XCD x again takes a contiguous range of that order.
 // When the padded M (mp, a multiple of 16) is not a multiple of the tile
-// height, the last m-tile (half) starts at mp - 256 (mp - 128) instead: it
-// overlaps the one before it, so every row it loads exists, and the rows
-// both compute get the same operands in the same order, so both store the
-// same values there.
+// height, the last m-tile (half) starts at mp - 256 (mp - 128) instead, and
+// when N is not a multiple of 256 the last n-tile starts at N - 256: such a
+// tile overlaps the one before it, so every row it loads exists and every
+// column it stores is < N, and the outputs both compute get the same
+// operands in the same order, so both store the same values there.
 struct InteriorPlan {
-    int tiles_m, nd, nwhole, group_m;
+    int tiles_m, tiles_n, nd, nwhole, group_m;
     int halves_m, nhalf, half_gm;
 };
 
@@ -319,6 +320,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
         (void)xcd_item(bid, P.nwhole, t);
         grouped_origin_bb<256, 256>(t, P.tiles_m, P.nd, P.group_m, n0, m0);
         m0 = m0 < mp - 256 ? m0 : mp - 256;
+        n0 = n0 < N - 256 ? n0 : N - 256;
         const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
         v16f acc[4][4];
         tile_mainloop<4>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
@@ -328,9 +330,10 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     }
     // nwhole is a multiple of 8: the half tiles' workgroups keep w % 8
     if (!xcd_item(bid - P.nwhole, P.nhalf, t)) return;
-    grouped_origin_bb<256, 128>(t, P.halves_m, (N >> 8) - P.nd, P.half_gm, n0, m0);
+    grouped_origin_bb<256, 128>(t, P.halves_m, P.tiles_n - P.nd, P.half_gm, n0, m0);
     m0 = m0 < mp - 128 ? m0 : mp - 128;
     n0 += P.nd * 256;
+    n0 = n0 < N - 256 ? n0 : N - 256;
     const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
     v16f acc[4][2];
     tile_mainloop<2>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
@@ -374,10 +377,10 @@ int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
 //  * the skinny kernel (16 weight rows per workgroup, K split over its
 //    waves) when padded M <= 64;
 //  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
-//    as half tiles when they fit one round) when N is a multiple of 256,
-//    padded M >= 256, K >= 512, N <= 2^21 and there are at least 64 tiles;
-//  * 256x256 edge-capable kernel when tiles cross N or padded M but there are
-//    still >= 256 of them;
+//    as half tiles when they fit one round) when N and padded M are
+//    >= 256, K >= 512, N < 2^21 and there are at least 64 tiles;
+//  * 256x256 edge-capable kernel when padded M < 256 but there are still
+//    >= 256 tiles;
 //  * 128x128 tiles when M_pad >= 128 and tiles times K chunks give >= 128
 //    workgroups;
 //  * 64x32 tiles otherwise (small M, few tiles).
@@ -387,7 +390,7 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     GemmPlan p = {};
     p.s = 1;
     const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
-    if (mp >= 256 && n % 256u == 0 && k >= 512u && n <= (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
+    if (mp >= 256 && n >= 256u && k >= 512u && n < (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
         p.kind = kGemmTiles;
         p.G = cus;
         const int tiles_m = ceil_div(mp, 256);
@@ -446,6 +449,7 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     const int tiles_m = ceil_div(mp, 256);
     InteriorPlan ip;
     ip.tiles_m = tiles_m;
+    ip.tiles_n = ceil_div((int)n, 256);
     ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
     ip.nd = p.workgroups / tiles_m;
     ip.group_m = tiles_m < 8 ? tiles_m : 8;

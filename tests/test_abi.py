@@ -149,13 +149,14 @@ def test_diagnostics_validation(L):
 def test_plans_cover_shapes(L):
     # every workload shape gets a plan whose tiles cover the output
     for m, n, k in [(16, 256, 512), (512, 3584, 3584), (512, 512, 3584), (2048, 18944, 3584),
-                    (2048, 3584, 18944), (4096, 18944, 3584), (1, 4608, 3584), (1000, 4608, 3584)]:
+                    (2048, 3584, 18944), (4096, 18944, 3584), (1, 4608, 3584), (1000, 4608, 3584),
+                    (2000, 18900, 3584), (200, 65636, 512)]:
         bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
         mp = rz.rz_pad_m(m)
         tiles = -(-mp // bm) * -(-n // bn)
-        interior = (bn, bm) == (256, 256) and mp >= 256 and n % 256 == 0 and k >= 512 and tiles >= 64
+        interior = (bn, bm) == (256, 256) and mp >= 256 and 256 <= n < 1 << 21 and k >= 512 and tiles >= 64
         if interior:
-            assert wgs == _interior_wgs(mp, n // 256, k)
+            assert wgs == _interior_wgs(mp, -(-n // 256), k)
         else:
             assert (bn, bm, wgs) == _edge_plan(m, n, k)[:3]
             assert wgs >= tiles

@@ -282,13 +282,18 @@ def _codes(g, shape):
     (300, 16384, 512, False),    # 3 halves per n-column: 0, 128 and 176
     (600, 25600, 512, False),    # 300 whole tiles, the last m-tile at 352
     (1000, 65536, 512, False),   # 4 whole rounds, the last m-tile at 752
+    # N not a multiple of 256: the last n-tile starts at N - 256
+    (2048, 2500, 1024, True),    # halves only; last n-tile at 2244
+    (2000, 18900, 512, False),   # ragged M and N: 2 rounds + halves, last tile at (1744, 18644)
+    (768, 25700, 512, False),    # 303 whole tiles, the last n-tile at 25444
+    (1000, 40000, 512, False),   # 2 rounds + 29 n-columns of 8 halves, ragged M and N
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
     from tests.test_abi import _interior_wgs
     mp = fp8_path.pad_m(m)
     bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
     assert (bn, bm, threads) == (256, 256, 256)
-    assert wgs == _interior_wgs(mp, n // 256, k)
+    assert wgs == _interior_wgs(mp, -(-n // 256), k)
     assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
     g = np.random.Generator(np.random.PCG64(m + n + k))
     a8, w8 = _codes(g, (mp, k)), _codes(g, (n, k))
@@ -305,6 +310,27 @@ def test_gemm_interior_plans(rz, m, n, k, full):
         assert y.shape == (m, n)
         err = np.abs(y[rows].astype(np.float64) - yr)
         assert (err <= tol).all(), f"{(err > tol).sum()} out of bound"
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (200, 65636, 512),   # padded M < 256 with 257 tiles: 256x256 tiles crossing M_pad and N
+    (129, 65400, 768),   # M_pad 144, last tile 120 columns wide
+])
+def test_gemm_large_edge(rz, m, n, k):
+    bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
+    mp = fp8_path.pad_m(m)
+    assert (bn, bm, threads, wgs) == (256, 256, 256, -(-n // 256))
+    assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
+    g = np.random.Generator(np.random.PCG64(m * 7 + n))
+    a8, w8 = _codes(g, (mp, k)), _codes(g, (n, k))
+    a8[m:] = 0
+    sc = np.array([1.0, 0.02, 0, 0], np.float32)
+    wdq = np.float32(0.013)
+    rows = np.unique(np.concatenate([[0, m - 1], g.choice(m, 40, replace=False)]))
+    yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
+    y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), float(wdq)))
+    err = np.abs(y[rows].astype(np.float64) - yr)
+    assert (err <= tol).all(), f"{(err > tol).sum()} out of bound"
 
 
 @pytest.mark.parametrize("m,n,k", [
