@@ -36,7 +36,7 @@ FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "gemm_common.h", "rz_internal.h")]
+                  for f in ("gemm.hip", "gemm_common.h", "rz_gemm.h")]
 
 
 def log(*a):

@@ -133,7 +133,8 @@ def rz_fp8_gemm_plan(m: int, n: int, k: int) -> tuple[int, int, int, int]:
 # ------------------------------------------------------------- entry points
 
 def rz_fp8_pack_weight(qtype: int, blocks, n: int, k: int, w_fp8=None, ws=None, stream=None):
-    """-> (w_fp8 uint8 [n][k], w_scale float, w_absmax float).  Syncs the stream."""
+    """-> (w_fp8 uint8 [n][k], w_scale float, w_absmax float).  Returns once the
+    scale is on the host; w_fp8 is complete for later work on the stream."""
     torch = _torch()
     _require_cuda(blocks, w_fp8, ws)
     dev = blocks.device

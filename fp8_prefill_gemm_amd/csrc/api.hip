@@ -122,12 +122,13 @@ const char* rz_last_error_string(void) { return g_last_error.c_str(); }
 const char* rz_version(void) { return "rz_fp8 0.1.0 gfx950"; }
 
 // Per-thread slot of fine-grained (coherent) pinned host memory that the
-// pack's encode kernel writes the scales into, so the host scale needs no
-// device-to-host copy, only the stream synchronisation.  Allocated on first
-// use, kept until the process ends; null if the allocation fails (then the
-// scales are copied back).  Calls on one thread are sequential (each one
-// synchronises its stream before returning), so one slot per thread is
-// enough.
+// pack's encode kernel writes the scales into, followed by the call's ticket
+// (below), so the host scale needs neither a device-to-host copy nor a
+// stream synchronisation.  Allocated on first use, kept until the process
+// ends; null if the allocation fails (then the scales are copied back and
+// the stream synchronised).  A call returns only after its kernel has
+// written its ticket, the slot's last write from that kernel, so one slot
+// per thread is enough.
 static float* host_scale_slot() {
     thread_local float* slot = nullptr;
     thread_local bool tried = false;
@@ -141,6 +142,23 @@ static float* host_scale_slot() {
         (void)hipGetLastError();  // a failed attempt leaves no error behind
     }
     return slot;
+}
+
+// Waits until `ticket` appears at *tag (written by the pack's encode kernel
+// with release order once the scales are in the slot).  The stream is
+// queried every 256 polls, so a stream that finishes, or fails, without
+// publishing the ticket ends the wait with an error instead of a hang.
+static hipError_t wait_for_ticket(const uint32_t* tag, uint32_t ticket, hipStream_t st) {
+    for (uint32_t i = 1;; ++i) {
+        if (__atomic_load_n(tag, __ATOMIC_ACQUIRE) == ticket) return hipSuccess;
+        if ((i & 255u) == 0) {
+            const hipError_t q = hipStreamQuery(st);
+            if (q == hipSuccess)
+                return __atomic_load_n(tag, __ATOMIC_ACQUIRE) == ticket ? hipSuccess : hipErrorUnknown;
+            if (q != hipErrorNotReady) return q;
+        }
+        __builtin_ia32_pause();
+    }
 }
 
 int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
@@ -157,20 +175,22 @@ int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, ui
     hipStream_t st = as_stream(stream);
     const uint64_t nb = (uint64_t)n * (k / 256u);
     float* slot = host_scale_slot();
+    thread_local uint32_t last_ticket = 0;
+    const uint32_t ticket = ++last_ticket == 0 ? ++last_ticket : last_ticket;  // never 0
     hipError_t e = rz::launch_pack(qtype, static_cast<const uint8_t*>(blocks), nb, w_fp8,
-                                   static_cast<uint8_t*>(ws), slot, st);
+                                   static_cast<uint8_t*>(ws), slot, ticket, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     float sc[4];
-    if (!slot) {  // no pinned slot: copy the scales back
+    if (slot) {
+        e = wait_for_ticket(reinterpret_cast<const uint32_t*>(slot) + 3, ticket, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        const volatile float* v = slot;  // written by the device before the ticket
+        for (int i = 0; i < 3; ++i) sc[i] = v[i];
+    } else {  // no pinned slot: copy the scales back
         e = hipMemcpyAsync(sc, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof sc,
                            hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
         if (e != hipSuccess) return hip_fail(e, fn);
-    }
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, fn);
-    if (slot) {
-        const volatile float* v = slot;  // written by the device
-        for (int i = 0; i < 4; ++i) sc[i] = v[i];
     }
     *w_scale_host = sc[2];
     if (w_absmax_host) *w_absmax_host = sc[0];

@@ -34,7 +34,7 @@
 // the workgroups that run together on one XCD share weight rows and
 // activation rows through that XCD's L2.
 #include "gemm_common.h"
-#include "rz_internal.h"
+#include "rz_gemm.h"
 
 namespace rz {
 namespace {

@@ -16,7 +16,7 @@
 // reads (8 or 16 consecutive rows, same chunk) and the stage writes hit
 // distinct banks.
 #include "gemm_common.h"
-#include "rz_internal.h"
+#include "rz_gemm.h"
 
 namespace rz {
 namespace {

@@ -131,8 +131,10 @@ __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(const uint8_t* __
 }
 
 // Pass 2: reduce the pass-1 keys, derive the scales, encode.  Workgroup 0
-// publishes {a, q, dq, 0} to scale_out and, when given, to host_out
-// (host-visible memory the caller reads after synchronising the stream).
+// publishes {a, q, dq, 0} to scale_out and, when given, {a, q, dq} to
+// host_out (coherent host memory) followed by `ticket` in its fourth word,
+// stored with release order at system scope: a host thread that sees the
+// ticket there can read the scales while the codes are still being written.
 template <int QT>
 __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __restrict__ blocks,
                                                                uint64_t nb,
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
                                                                int npartial,
                                                                uint8_t* __restrict__ w_fp8,
                                                                float* __restrict__ scale_out,
-                                                               float* __restrict__ host_out) {
+                                                               float* __restrict__ host_out, uint32_t ticket) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
     __shared__ uint32_t red[kThreads / kWave];
     const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
             host_out[0] = sc.a;
             host_out[1] = sc.q;
             host_out[2] = sc.dq;
-            host_out[3] = 0.0f;
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(host_out) + 3, ticket, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
     const float q = sc.q;
@@ -218,17 +221,17 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nb, flo
 }
 
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint8_t* w_fp8, uint8_t* ws,
-                       float* host_scale, hipStream_t st) {
+                       float* host_scale, uint32_t ticket, hipStream_t st) {
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
     const int g1 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
     const int g2 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
     if (qtype == 12) {
         pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale);
+        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale, ticket);
     } else {
         pack_absmax_kernel<14><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale);
+        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale, ticket);
     }
     return hipGetLastError();
 }

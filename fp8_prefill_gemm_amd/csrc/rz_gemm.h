@@ -1,0 +1,34 @@
+// Host-side GEMM plan and launchers (gemm.hip, gemm_edge.hip), shared with
+// the C ABI layer.  Every launcher assumes its arguments were validated by
+// the caller (api.hip) and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rz {
+
+enum GemmKind { kGemmTiles = 0, kGemmMedium = 1, kGemmSmall = 2, kGemmLargeEdge = 3, kGemmSkinny = 4, kGemmGemv = 5 };
+struct GemmPlan {
+    int bn, bm, threads, workgroups, kind;
+    // interior-tile plan: CUs, whole-tile rounds, tiles left over (run as
+    // half tiles), workgroups for those half tiles
+    int G, R, rem, half_workgroups;
+    // edge-capable plans: K chunks per tile (1: no split)
+    int s;
+    size_t ws_bytes;  // workspace the plan needs (0: none)
+};
+GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed);
+hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
+                       uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
+                       size_t ws_bytes, int cus, hipStream_t st);
+// The kernels of every plan kind but kGemmTiles (gemm_edge.hip); ws holds
+// the split-K counters and partial sums when p.s > 1.
+hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
+                            uint32_t k, const float* act_scale, float w_scale, float* y, void* ws, hipStream_t st);
+// Split-K workspace: arrival counters of the split tiles (one uint32 each),
+// padded to 256 bytes; the partial sums follow.
+inline size_t split_counter_bytes(int tiles) { return ((size_t)tiles * sizeof(unsigned) + 255) / 256 * 256; }
+
+}  // namespace rz

@@ -18,7 +18,8 @@
  *     caller; *_host is host memory owned by the caller.  The library keeps
  *     no persistent device allocation of its own.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     All work is ordered on it.  Only rz_fp8_pack_weight synchronises it.
+ *     All work is ordered on it.  No call synchronises it; only
+ *     rz_fp8_pack_weight waits on the host, for its scale (below).
  *   - Arguments are validated before anything is launched.  Errors return a
  *     negative rz_status and leave outputs untouched; nothing aborts.
  *     rz_last_error_string() gives a message for the calling thread.
@@ -88,8 +89,12 @@ size_t rz_workspace_bytes(void);
  *   w_scale_host  host out, RN(a'/448): the weight's dequantisation scale
  *   w_absmax_host host out (may be NULL): a
  *   ws            device workspace of rz_workspace_bytes()
- * The dequantised fp32 weight is never materialised.  Synchronises `stream`
- * once, to return the scale to the host.
+ * The dequantised fp32 weight is never materialised.  Returns once the
+ * scale is known on the host: the second kernel publishes it to pinned host
+ * memory before it encodes, and the call waits for that, not for the codes.
+ * w_fp8 is complete for later work on `stream`; other streams and the host
+ * must synchronise `stream` before reading it.  If the stream ends or fails
+ * without publishing the scale, the call returns RZ_ERR_HIP.
  */
 int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k,
                        uint8_t* w_fp8, float* w_scale_host, float* w_absmax_host,
