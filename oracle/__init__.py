@@ -17,6 +17,8 @@ Modules:
   kquant   — Q4_K / Q6_K super-block dequantisation to fp32
   fp8_path — absmax, scales, weight packing, activation quantisation,
              exact FP8 GEMM, fused epilogue and the parity error bound
+  kquant_gemv — the small-M GEMV straight from K-quant blocks (fp32 input
+             and output) and its fp32-accumulation error bound
 
 Parity status: every function is pinned by tests under ``tests/`` that do
 not re-derive it (fixed points, closed forms, exhaustive sweeps, a library
