@@ -163,6 +163,64 @@ def pack_model(args, dev) -> int:
     return 0
 
 
+def small_m(args, dev) -> int:
+    """Small batches at K=3584, N=4608, Q4_K (one line): the GEMV straight from
+    the K-quant blocks against the FP8 path (activation quantisation + FP8
+    GEMM on the packed weight), warm, HIP events around 200 launches each."""
+    import numpy as np
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    n, k, reps = 4608, 3584, 200
+    stream = torch.cuda.current_stream(dev)
+    blocks = torch.from_numpy(W.weight_blocks(W.Q4_K, W.seed_for(5, 0, "up"), n, k)).to(dev)
+    w8 = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    ws = rz.workspace(dev)
+    _, w_scale, _ = rz.rz_fp8_pack_weight(W.Q4_K, blocks, n, k, w8, ws, stream)
+    kq_bytes = blocks.numel()
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    rows = {}
+    for m in args.small_m:
+        x = torch.from_numpy(W.act_student_t(W.seed_for(5, 0, "x_ffn") + m, m, k)).to(dev)
+        a8 = torch.empty((rz.rz_pad_m(m), k), dtype=torch.uint8, device=dev)
+        sc = torch.empty(2, dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        row = {}
+        if m <= rz.KGEMV_MAX_M:
+            t = timed(lambda: rz.rz_kquant_gemv(W.Q4_K, blocks, n, k, x, y, stream))
+            b = kq_bytes + 4 * m * k + 4 * m * n
+            row["kquant_gemv"] = {"us": round(t * 1e6, 2), "bytes": b, "gb_s": round(b / t / 1e9, 1),
+                                  "hbm_frac": round(b / t / 1e12 / HBM_PEAK_TBPS, 4)}
+        rz.rz_fp8_quant_act(x, a8, sc, ws, stream)
+        t = timed(lambda: rz.rz_fp8_gemm(a8, w8, m, sc, w_scale, y, stream))
+        b = n * k + rz.rz_pad_m(m) * k + 4 * m * n
+        row["fp8_gemm"] = {"us": round(t * 1e6, 2), "bytes": b, "gb_s": round(b / t / 1e9, 1)}
+        t = timed(lambda: (rz.rz_fp8_quant_act(x, a8, sc, ws, stream),
+                           rz.rz_fp8_gemm(a8, w8, m, sc, w_scale, y, stream)))
+        row["fp8_quant_plus_gemm_us"] = round(t * 1e6, 2)
+        rows[str(m)] = row
+        log(f"m={m}: {row}")
+    out = {"metric": "small-batch matmul at K=3584, N=4608, Q4_K weight (warm)", "unit": "us",
+           "higher_is_better": False, "rows": rows, "kquant_bytes": kq_bytes, "data": "synthetic",
+           "config": {"workload": "edge configuration: N=4608, K=3584, Q4_K; Student-t(3) activations "
+                                  "with 8 channels x100", "m": list(args.small_m)}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +233,8 @@ def main() -> int:
     ap.add_argument("--pack-model", action="store_true",
                     help="time the cold-cache packing of all 196 weights of the 28-layer sweep instead")
     ap.add_argument("--pack-repeats", type=int, default=3, help="cold passes of --pack-model")
+    ap.add_argument("--small-m", type=int, nargs="*", default=None,
+                    help="instead time the small-batch paths at N=4608, K=3584 (Q4_K) for these m")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -198,6 +258,10 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.pack_model:
         return pack_model(args, dev)
+    if args.small_m is not None:
+        if not args.small_m:
+            args.small_m = [1, 2, 3, 4, 8, 37]
+        return small_m(args, dev)
 
     ffn, down = W.config_groups(3)
     gate, up = ffn.gemms

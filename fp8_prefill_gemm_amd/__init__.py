@@ -48,6 +48,7 @@ _SIGS = {
     "rz_e4m3_encode": (_i32, [_vp, _u64, _f32, _vp, _vp]),
     "rz_fp8_scales": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_fp8_gemm_plan": (_i32, [_u32, _u32, _u32, _vp]),
+    "rz_kquant_gemv": (_i32, [_i32, _vp, _u32, _u32, _vp, _u32, _vp, _vp]),
     "rz_status_string": (ctypes.c_char_p, [_i32]),
     "rz_last_error_string": (ctypes.c_char_p, []),
     "rz_version": (ctypes.c_char_p, []),
@@ -204,6 +205,21 @@ def rz_fp8_gemm(a_fp8, w_fp8, m: int, act_scale, w_scale: float, y=None, stream=
     _require_cuda(ws)
     _check(lib().rz_fp8_gemm(_ptr(a_fp8), _ptr(w_fp8), m, n, k, _ptr(act_scale), float(w_scale),
                              _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, dev)))
+    return y
+
+
+KGEMV_MAX_M = 8
+
+
+def rz_kquant_gemv(qtype: int, blocks, n: int, k: int, x, y=None, stream=None):
+    """-> y fp32 [m][n] = x @ dequant(blocks)^T, straight from the K-quant
+    blocks (x fp32 [m][k], 1 <= m <= KGEMV_MAX_M)."""
+    torch = _torch()
+    _require_cuda(blocks, x, y)
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=blocks.device)
+    _check(lib().rz_kquant_gemv(qtype, _ptr(blocks), n, k, _ptr(x), m, _ptr(y), _stream(stream, blocks.device)))
     return y
 
 

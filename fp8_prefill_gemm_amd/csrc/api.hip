@@ -254,6 +254,23 @@ int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out) {
     return RZ_OK;
 }
 
+int rz_kquant_gemv(int qtype, const void* blocks, uint32_t n, uint32_t k, const float* x, uint32_t m,
+                   float* y, void* stream) {
+    static const char* fn = "rz_kquant_gemv";
+    if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
+    if (int r = check_k(fn, k)) return r;
+    if (m > RZ_KGEMV_MAX_M) return fail(RZ_ERR_SHAPE, "%s: m=%u exceeds %u", fn, m, (unsigned)RZ_KGEMV_MAX_M);
+    if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
+    if (!blocks || !x || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS || n > 0x7FFFFFF0u) return fail(RZ_ERR_SHAPE, "%s: n*k too large", fn);
+    if (!aligned16(blocks) || !aligned16(x) || !aligned16(y))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_kquant_gemv(qtype, static_cast<const uint8_t*>(blocks), n, k, x, m, y,
+                                          as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
 int rz_dequant_f32(int qtype, const void* blocks, uint32_t n, uint32_t k, float* out_dev,
                    void* stream) {
     static const char* fn = "rz_dequant_f32";

@@ -150,6 +150,34 @@ int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t
  * (0 when it would not split). */
 size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k);
 
+/* Largest batch rz_kquant_gemv accepts. */
+#define RZ_KGEMV_MAX_M 8u
+
+/*
+ * Batched GEMV straight from the K-quant weight, for small batches
+ * (cublas_prefill/mod.rs page, the note on cublas_gemm_threshold: below a
+ * threshold of 4 rows by default the pages run GEMV kernels instead of the
+ * FP8 GEMM; q6k_gemv_indexed.rs page, the q4k_gemv_into and
+ * q6k_gemv_indexed_async dispatchers, fp32 in, K-quant weight, fp32 out):
+ *
+ *   y[i][j] = sum_kk x[i][kk] * w[j][kk]        for i < m, j < n
+ *
+ * where w is the weight decoded exactly as rz_dequant_f32 decodes it.  No
+ * FP8 conversion and no scales are involved; nothing is packed or cached.
+ *
+ *   blocks  device, n*(k/256) super-blocks, row-major as for
+ *           rz_fp8_pack_weight (read once, at 0.5625 / 0.8203 B per weight)
+ *   x       device, fp32 [m][k] row-major
+ *   y       device out, fp32 [m][n] row-major
+ * 1 <= m <= RZ_KGEMV_MAX_M (RZ_ERR_SHAPE otherwise; m == 0 or n == 0 is a
+ * no-op and any pointer may then be NULL).  Products are exact fp32
+ * multiply-adds accumulated in fp32, so each output is within
+ * gamma_k * sum_kk |x[i][kk] * w[j][kk]| of the exact sum (gamma_k =
+ * k u / (1 - k u), u = 2^-24).  No workspace, no host synchronisation.
+ */
+int rz_kquant_gemv(int qtype, const void* blocks, uint32_t n, uint32_t k, const float* x,
+                   uint32_t m, float* y, void* stream);
+
 /* ---------------------------------------------------------------------
  * Diagnostics: the individual steps, exposed so that each can be checked
  * against the oracle.  Same conventions as above.

@@ -114,6 +114,27 @@ def test_gemm_validation(L):
     assert f(None, None, 0, 8, 255, None, 1.0, None) == RZ_ERR_SHAPE
 
 
+def test_kquant_gemv_validation(L):
+    def f(q, b, n, k, x, m, y):
+        return L.rz_kquant_gemv(q, b, n, k, x, m, y, None)
+    assert f(12, None, 8, 256, P2, 1, P3) == RZ_ERR_NULL
+    assert f(14, P, 8, 256, None, 1, P3) == RZ_ERR_NULL
+    assert f(12, P, 8, 256, P2, 1, None) == RZ_ERR_NULL
+    assert f(2, P, 8, 256, P2, 1, P3) == RZ_ERR_QTYPE
+    assert f(12, P, 8, 300, P2, 1, P3) == RZ_ERR_SHAPE
+    assert f(12, P, 8, 0, P2, 1, P3) == RZ_ERR_SHAPE
+    assert f(12, P, 8, 256, P2, 9, P3) == RZ_ERR_SHAPE
+    assert "exceeds 8" in _err(L)
+    assert f(12, P, 1 << 30, 1 << 10, P2, 1, P3) == RZ_ERR_SHAPE
+    assert f(12, BAD, 8, 256, P2, 1, P3) == RZ_ERR_ALIGN
+    assert f(14, P, 8, 256, BAD, 1, P3) == RZ_ERR_ALIGN
+    assert f(14, P, 8, 256, P2, 1, BAD) == RZ_ERR_ALIGN
+    # empty products are no-ops that touch nothing (no device needed)
+    assert f(12, None, 8, 256, None, 0, None) == RZ_OK
+    assert f(14, None, 0, 256, None, 4, None) == RZ_OK
+    assert f(12, None, 0, 255, None, 4, None) == RZ_ERR_SHAPE
+
+
 def test_gemm_workspace_sizes(L):
     # the GEMV and skinny kernels (padded M <= 64) need none; split-K with 64x32 tiles:
     # 256 bytes of arrival counters + 12 tiles x 2 chunks of 64x32 fp32
