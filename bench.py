@@ -213,7 +213,22 @@ def small_m(args, dev) -> int:
         row["fp8_quant_plus_gemm_us"] = round(t * 1e6, 2)
         rows[str(m)] = row
         log(f"m={m}: {row}")
+    # the down projection's Q6_K weight (N=3584, K=18944) at the same batch sizes
+    nd, kd = 3584, 18944
+    dblocks = torch.from_numpy(W.weight_blocks(W.Q6_K, W.seed_for(3, 0, "down"), nd, kd)).to(dev)
+    q6 = {}
+    for m in args.small_m:
+        if m > rz.KGEMV_MAX_M:
+            continue
+        x = torch.from_numpy(W.act_silu_gated(W.seed_for(3, 0, "x_down") + m, m, kd)).to(dev)
+        y = torch.empty((m, nd), dtype=torch.float32, device=dev)
+        t = timed(lambda: rz.rz_kquant_gemv(W.Q6_K, dblocks, nd, kd, x, y, stream))
+        b = dblocks.numel() + 4 * m * kd + 4 * m * nd
+        q6[str(m)] = {"us": round(t * 1e6, 2), "bytes": b, "gb_s": round(b / t / 1e9, 1),
+                      "hbm_frac": round(b / t / 1e12 / HBM_PEAK_TBPS, 4)}
+        log(f"q6k down m={m}: {q6[str(m)]}")
     out = {"metric": "small-batch matmul at K=3584, N=4608, Q4_K weight (warm)", "unit": "us",
+           "kquant_gemv_q6k_down_n3584_k18944": q6,
            "higher_is_better": False, "rows": rows, "kquant_bytes": kq_bytes, "data": "synthetic",
            "config": {"workload": "edge configuration: N=4608, K=3584, Q4_K; Student-t(3) activations "
                                   "with 8 channels x100", "m": list(args.small_m)}}

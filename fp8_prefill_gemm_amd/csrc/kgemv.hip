@@ -10,17 +10,23 @@
 //     y[i][j] = sum_kk x[i][kk] * w[j][kk],   w = the K-quant weight decoded
 //                                             to fp32 (correctly rounded)
 //
-// Design (gfx950, wave64): the weight is read once, at its K-quant size
+// Design (gfx950, wave64).  The weight is read once, at its K-quant size
 // (0.5625 B per Q4_K weight, 0.8203 B per Q6_K weight), and never written
-// back decoded.  One wave owns RW consecutive weight rows.  Lane l takes a
-// fixed piece of every super-block it visits (Q4_K: 16-byte quant slice
-// l % 8 of block l / 8, 32 weights; Q6_K: quarter l % 4 of block l / 4, 64
-// weights), so the activation values a lane needs are the same for all RW
-// rows: each is loaded once per block and used RW times.  Every weight is
-// decoded exactly as the dequantisation defines it (one rounding) and
-// multiplied into its row's fp32 sums with fused multiply-adds, one sum per
-// (row, batch row) per lane, in K order; a butterfly over the wave adds the
-// 64 lane sums.  No workspace, no atomics, no LDS.
+// back decoded.  Eight lanes share a super-block, 32 weights each (Q4_K:
+// one 16-byte quant slice; Q6_K: one 16-byte ql run with its qh bits), so a
+// wave covers eight blocks per step.  A workgroup of WAVES waves owns
+// WAVES * RW consecutive rows and walks K in chunks of CB blocks:
+//   1. every lane issues the loads of its pieces of the chunk for its RW
+//      rows (all of them before any is used);
+//   2. the workgroup copies the chunk of the activation (all batch rows)
+//      into LDS, permuted so that the 32 values a lane needs are contiguous:
+//      one 144-byte slot per (block, lane), so the eight 16-byte reads of a
+//      slot by the 64 lanes of a wave hit distinct banks;
+//   3. each lane decodes its pieces exactly as the dequantisation defines
+//      them (one rounding) and multiplies them into its (row, batch row)
+//      fp32 sums with fused multiply-adds, in K order; each activation value
+//      read from LDS serves RW rows.
+// A butterfly over the wave adds the 64 lane sums.  No workspace, no atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,9 +35,6 @@
 
 namespace rz {
 namespace {
-
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -63,17 +66,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ void load_x16(const float* __restrict__ p, float (&o)[16]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * i);
-        o[4 * i] = v.x;
-        o[4 * i + 1] = v.y;
-        o[4 * i + 2] = v.z;
-        o[4 * i + 3] = v.w;
-    }
-}
-
 // Writes the RW x MR wave sums: lane 0 stores y[mi][r0 + i] for rows < n.
 template <int RW, int MR>
 __device__ __forceinline__ void store_sums(float (&acc)[RW][MR], uint32_t r0, uint32_t n, float* __restrict__ y) {
@@ -87,25 +79,131 @@ __device__ __forceinline__ void store_sums(float (&acc)[RW][MR], uint32_t r0, ui
         }
 }
 
-// ---------------------------------------------------------------- Q4_K
-//
-// Lane l: slice s = l % 8 of block b = l / 8 (+ 8 per step).  The slice's 16
-// quant bytes hold the low nibbles of elements 64c + 16h + t and the high
-// nibbles of elements 64c + 32 + 16h + t (c = s / 2, h = s % 2, t < 16).
-template <int MR, int RW>
-__global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(const uint8_t* __restrict__ blocks, uint32_t n,
-                                                               uint32_t nb, const float* __restrict__ x,
-                                                               uint32_t k, float* __restrict__ y) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t r0 = (blockIdx.x * kGemvWaves + threadIdx.x / kWave) * RW;
-    if (r0 >= n) return;  // whole waves leave; no barriers below
-    const int s = lane & 7;
-    const int xoff = 64 * (s >> 1) + 16 * (s & 1);
+constexpr int kLanesPerBlock = 8;                          // 32 weights per lane
+constexpr int kBlocksPerStep = kWave / kLanesPerBlock;     // blocks a wave covers per step
+constexpr int kSlotFloats = 36;                            // 32 values + 4 pad: slots 144 B apart
+constexpr int kBlockFloats = kLanesPerBlock * kSlotFloats; // LDS floats per block and batch row
+
+// Where element e (0..255) of a super-block lives in the LDS slots: lane
+// (slot) u of the block and position in the slot.  Four consecutive elements
+// starting at a multiple of 4 stay consecutive.
+//   Q4_K: quant byte 32c + l holds element 64c + l (low nibble) and
+//         64c + 32 + l (high nibble); lane u = 2c + l/16 takes bytes
+//         32c + 16(u%2) .. +15: low nibbles at positions 0..15, high 16..31.
+//   Q6_K: in half h, ql byte l / 32 + l (l < 32) and qh byte l give elements
+//         l + 32p (p < 4: low nibble of ql[l], low nibble of ql[32+l], high
+//         nibble of ql[l], high nibble of ql[32+l], with qh bits 2p..2p+1);
+//         lane u = 4h + 2(l/16) + p%2 takes the ql run of p%2, runs p = p%2
+//         (positions 0..15) and p%2 + 2 (positions 16..31).
+template <int Q>
+__device__ __forceinline__ int slot_of(int e, int& pos) {
+    if constexpr (Q == 12) {
+        const int c = e >> 6, w = e & 63, hi = w >> 5, l = w & 31;
+        pos = 16 * hi + (l & 15);
+        return 2 * c + (l >> 4);
+    } else {
+        const int h = e >> 7, w = e & 127, p = w >> 5, l = w & 31;
+        pos = 16 * (p >> 1) + (l & 15);
+        return 4 * h + 2 * (l >> 4) + (p & 1);
+    }
+}
+
+// The raw bytes one lane needs from one block.
+template <int Q>
+struct Raw;
+template <>
+struct Raw<12> {
+    uint4 head, qs;
+};
+template <>
+struct Raw<14> {
+    uint4 ql, qh;
+    uint32_t sc, d;  // sc: the run's two int8 scales in bytes 0 and 1; d: f16 bits
+};
+
+__device__ __forceinline__ void load_raw(const uint8_t* blk, int u, Raw<12>& r) {
+    r.head = ld16(blk);
+    r.qs = ld16(blk + 16 + 16 * u);
+}
+
+// Q6_K blocks are 210 bytes, so they start 2-byte aligned: the 16-byte ql and
+// qh runs are read with ld16_a2 (furthest byte: 2 past the qh run, inside
+// the block), the two scales and d with byte and half-word loads.
+__device__ __forceinline__ void load_raw(const uint8_t* blk, int u, Raw<14>& r) {
+    const int h = u >> 2, l0 = 16 * ((u >> 1) & 1), odd = u & 1;
+    r.ql = ld16_a2(blk + 64 * h + 32 * odd + l0);
+    r.qh = ld16_a2(blk + 128 + 32 * h + l0);
+    const int si = 192 + 8 * h + (l0 >> 4) + 2 * odd;
+    r.sc = (uint32_t)blk[si] | ((uint32_t)blk[si + 4] << 8);
+    r.d = *reinterpret_cast<const uint16_t*>(blk + 208);
+}
+
+// Decode a lane's 32 weights into slot order (w[pos]).
+__device__ __forceinline__ void decode_raw(const Raw<12>& r, int u, float (&w)[32]) {
+    Q4Unit q;
+    q4k_decode_unit(r.head, r.qs, u, q);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        w[t] = q.lo[t];
+        w[16 + t] = q.hi[t];
+    }
+}
+
+// value = (d*sc)*(q-32): exact in fp32 (at most 24 significant bits).  With a
+// finite d it is computed as one fused multiply-add d*sc*q - 32*d*sc (exact,
+// so equal); an infinite or NaN d takes the product form, as the definition.
+template <bool kFinite>
+__device__ __forceinline__ void q6k_decode_run2(const Raw<14>& r, int shA, float (&w)[32]) {
+    const float d = half_bits_to_float(r.d);
+    const float dsA = d * (float)(int8_t)(r.sc & 0xFFu);
+    const float dsB = d * (float)(int8_t)((r.sc >> 8) & 0xFFu);
+    const uint32_t L[4] = {r.ql.x, r.ql.y, r.ql.z, r.ql.w};
+    const uint32_t H[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t a = (L[i] & 0x0F0F0F0Fu) | (((H[i] >> shA) & 0x03030303u) << 4);
+        uint32_t b = ((L[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> (shA + 4)) & 0x03030303u) << 4);
+        asm("" : "+v"(a), "+v"(b));  // byte b converts with v_cvt_f32_ubyte<b>
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+            const float qa = (float)((a >> (8 * bt)) & 0xFFu), qb = (float)((b >> (8 * bt)) & 0xFFu);
+            w[4 * i + bt] = kFinite ? __builtin_fmaf(dsA, qa, -32.0f * dsA) : dsA * (qa - 32.0f);
+            w[16 + 4 * i + bt] = kFinite ? __builtin_fmaf(dsB, qb, -32.0f * dsB) : dsB * (qb - 32.0f);
+        }
+    }
+}
+
+__device__ __forceinline__ void decode_raw(const Raw<14>& r, int u, float (&w)[32]) {
+    const int shA = 2 * (u & 1);
+    if (half_finite(r.d))
+        q6k_decode_run2<true>(r, shA, w);
+    else
+        q6k_decode_run2<false>(r, shA, w);
+}
+
+template <int Q>
+constexpr int block_bytes() {
+    return Q == 12 ? kQ4Bytes : kQ6Bytes;
+}
+
+template <int Q, int MR, int RW, int CB, int WAVES>
+__global__ __launch_bounds__(WAVES* kWave) void kgemv_kernel(const uint8_t* __restrict__ blocks, uint32_t n,
+                                                             uint32_t nb, const float* __restrict__ x, uint32_t k,
+                                                             float* __restrict__ y) {
+    constexpr int kThreads = WAVES * kWave;
+    constexpr int J = CB / kBlocksPerStep;  // steps per chunk
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // [MR][CB][kBlockFloats]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int u = lane & (kLanesPerBlock - 1);  // lane within its block
+    const int bl = lane / kLanesPerBlock;       // block within a step
+    const uint32_t r0 = (blockIdx.x * WAVES + tid / kWave) * RW;
+    const bool active = r0 < n;  // inactive waves still take part in staging and barriers
     const uint8_t* rowp[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
         const uint32_t r = (r0 + i < n) ? r0 + i : n - 1;  // rows past n re-read the last row, not stored
-        rowp[i] = blocks + (size_t)r * nb * kQ4Bytes + 16 * s;
+        rowp[i] = blocks + (size_t)r * nb * block_bytes<Q>();
     }
     float acc[RW][MR];
 #pragma unroll
@@ -113,131 +211,110 @@ __global__ __launch_bounds__(kGemvThreads) void q4k_gemv_kernel(const uint8_t* _
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi) acc[i][mi] = 0.0f;
 
-    for (uint32_t b = lane >> 3; b < nb; b += 8) {
-        Q4Unit u[RW];
+    // weight loads of a chunk (blocks past the chunk re-read its first block)
+    auto load_chunk = [&](Raw<Q> (&raw)[J][RW], uint32_t cb0, int nbc) {
 #pragma unroll
-        for (int i = 0; i < RW; ++i) {
-            const uint8_t* blk = rowp[i] + (size_t)b * kQ4Bytes;
-            const uint4 head = ld16(blk - 16 * s);
-            const uint4 qs = ld16(blk + 16);
-            q4k_decode_unit(head, qs, s, u[i]);
+        for (int j = 0; j < J; ++j) {
+            const int b = bl + kBlocksPerStep * j;
+            const uint32_t blk = cb0 + (b < nbc ? b : 0);
+#pragma unroll
+            for (int i = 0; i < RW; ++i) load_raw(rowp[i] + (size_t)blk * block_bytes<Q>(), u, raw[j][i]);
         }
-        const float* xb = x + (size_t)b * kQK + xoff;
+    };
+    auto chunk_len = [&](uint32_t cb0) { return (nb - cb0) < (uint32_t)CB ? (int)(nb - cb0) : CB; };
+
+    for (uint32_t cb0 = 0; cb0 < nb; cb0 += CB) {
+        const int nbc = chunk_len(cb0);
+        Raw<Q> raw[J][RW];
+        if (active) load_chunk(raw, cb0, nbc);  // in flight while the activation is staged
+        // the activation chunk into the LDS slots
+        const int pieces = nbc * (kQK / 4);
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi) {
-            float xl[16], xh[16];
-            load_x16(xb + (size_t)mi * k, xl);
-            load_x16(xb + (size_t)mi * k + 32, xh);
-#pragma unroll
-            for (int i = 0; i < RW; ++i) {
-                float a = acc[i][mi];
-#pragma unroll
-                for (int t = 0; t < 16; ++t) a = __builtin_fmaf(u[i].lo[t], xl[t], a);
-#pragma unroll
-                for (int t = 0; t < 16; ++t) a = __builtin_fmaf(u[i].hi[t], xh[t], a);
-                acc[i][mi] = a;
+            const float* src = x + (size_t)mi * k + (size_t)cb0 * kQK;
+            for (int pc = tid; pc < pieces; pc += kThreads) {
+                int pos;
+                const int sl = slot_of<Q>((pc & 63) * 4, pos);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * pc);
+                *reinterpret_cast<f32x4*>(xs + (mi * CB + (pc >> 6)) * kBlockFloats + sl * kSlotFloats + pos) = v;
             }
         }
-    }
-    store_sums<RW, MR>(acc, r0, n, y);
-}
-
-// ---------------------------------------------------------------- Q6_K
-//
-// Lane l: quarter q = l % 4 of block b = l / 4 (+ 16 per step), i.e. half
-// h = q / 2 and l0 = 16 (q % 2): the runs of 16 elements 128h + 32p + l0 + t
-// (p < 4).  A block is 210 bytes, so blocks start 2-byte aligned; its 16-byte
-// fields are read with ld16_a2.  The furthest byte read is 2 past the end of
-// the 16 scale bytes (offset 208), inside the block.
-template <int MR, int RW>
-__global__ __launch_bounds__(kGemvThreads) void q6k_gemv_kernel(const uint8_t* __restrict__ blocks, uint32_t n,
-                                                               uint32_t nb, const float* __restrict__ x,
-                                                               uint32_t k, float* __restrict__ y) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t r0 = (blockIdx.x * kGemvWaves + threadIdx.x / kWave) * RW;
-    if (r0 >= n) return;
-    const int q = lane & 3;
-    const int h = q >> 1, l0 = 16 * (q & 1);
-    const int xoff = 128 * h + l0;
-    const uint8_t* rowp[RW];
+        __syncthreads();
+        // decode and multiply
+        if (active) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-        const uint32_t r = (r0 + i < n) ? r0 + i : n - 1;
-        rowp[i] = blocks + (size_t)r * nb * kQ6Bytes;
-    }
-    float acc[RW][MR];
+            for (int j = 0; j < J; ++j) {
+                const int b = bl + kBlocksPerStep * j;
+                if (b < nbc) {
+                    float w[RW][32];
 #pragma unroll
-    for (int i = 0; i < RW; ++i)
+                    for (int i = 0; i < RW; ++i) decode_raw(raw[j][i], u, w[i]);
+                    const float* xl = xs + b * kBlockFloats + u * kSlotFloats;
 #pragma unroll
-        for (int mi = 0; mi < MR; ++mi) acc[i][mi] = 0.0f;
-
-    for (uint32_t b = lane >> 2; b < nb; b += 16) {
-        Q6Unit u[RW];
+                    for (int mi = 0; mi < MR; ++mi) {
+                        float xv[32];
 #pragma unroll
-        for (int i = 0; i < RW; ++i) {
-            const uint8_t* blk = rowp[i] + (size_t)b * kQ6Bytes;
-            const uint4 ql_a = ld16_a2(blk + 64 * h + l0);
-            const uint4 ql_b = ld16_a2(blk + 64 * h + 32 + l0);
-            const uint4 qh = ld16_a2(blk + 128 + 32 * h + l0);
-            const uint4 sc = ld16_a2(blk + 192);
-            const uint32_t dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
-            const int base = 8 * h + (l0 >> 4);
-            const uint32_t sc4 = byte_of(sc, base) | (byte_of(sc, base + 2) << 8) | (byte_of(sc, base + 4) << 16) |
-                                 (byte_of(sc, base + 6) << 24);
-            if (half_finite(dbits))
-                q6k_decode_unit<true>(ql_a, ql_b, qh, sc4, dbits, u[i]);
-            else
-                q6k_decode_unit<false>(ql_a, ql_b, qh, sc4, dbits, u[i]);
-        }
-        const float* xb = x + (size_t)b * kQK + xoff;
+                        for (int c = 0; c < 8; ++c) {
+                            const f32x4 t4 = *reinterpret_cast<const f32x4*>(xl + mi * CB * kBlockFloats + 4 * c);
+                            xv[4 * c] = t4.x;
+                            xv[4 * c + 1] = t4.y;
+                            xv[4 * c + 2] = t4.z;
+                            xv[4 * c + 3] = t4.w;
+                        }
 #pragma unroll
-        for (int mi = 0; mi < MR; ++mi) {
+                        for (int i = 0; i < RW; ++i) {
+                            float a = acc[i][mi];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float xv[16];
-                load_x16(xb + (size_t)mi * k + 32 * p, xv);
-#pragma unroll
-                for (int i = 0; i < RW; ++i) {
-                    float a = acc[i][mi];
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) a = __builtin_fmaf(u[i].v[p][t], xv[t], a);
-                    acc[i][mi] = a;
+                            for (int t = 0; t < 32; ++t) a = __builtin_fmaf(w[i][t], xv[t], a);
+                            acc[i][mi] = a;
+                        }
+                    }
                 }
             }
         }
+        __syncthreads();  // the next chunk overwrites the slots
     }
-    store_sums<RW, MR>(acc, r0, n, y);
+    if (active) store_sums<RW, MR>(acc, r0, n, y);
 }
 
-template <int MR, int RW>
+// Launch shape (measured at N=4608, K=3584 Q4_K and N=3584, K=18944 Q6_K,
+// m = 1 and 4): chunks of 8 blocks (LDS = MR * 9216 B); 4 waves per group,
+// 8 for Q6_K at m >= 3; one row per wave except Q4_K at m >= 3 with
+// n >= 4096, where two rows per wave halve the activation reads from LDS.
+constexpr int kChunkBlocks = 8;
+
+template <int Q, int MR, int RW, int WAVES>
+hipError_t launch_q(const uint8_t* blocks, uint32_t n, uint32_t nb, const float* x, uint32_t k, float* y,
+                    hipStream_t st) {
+    constexpr size_t lds = (size_t)MR * kChunkBlocks * kBlockFloats * sizeof(float);
+    auto kern = kgemv_kernel<Q, MR, RW, kChunkBlocks, WAVES>;
+    if constexpr (lds > 65536) {  // m = 8: 72 KB of the 160 KB per CU, opted in once per kernel
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess) return attr;
+    }
+    const uint32_t waves = (n + RW - 1) / RW;
+    const dim3 grid((waves + WAVES - 1) / WAVES), block(WAVES * kWave);
+    kern<<<grid, block, lds, st>>>(blocks, n, nb, x, k, y);
+    return hipGetLastError();
+}
+
+template <int MR>
 hipError_t launch_mr(int qtype, const uint8_t* blocks, uint32_t n, uint32_t nb, const float* x, uint32_t k,
                      float* y, hipStream_t st) {
-    const uint32_t waves = (n + RW - 1) / RW;
-    const dim3 grid((waves + kGemvWaves - 1) / kGemvWaves), block(kGemvThreads);
-    if (qtype == 12)
-        q4k_gemv_kernel<MR, RW><<<grid, block, 0, st>>>(blocks, n, nb, x, k, y);
-    else
-        q6k_gemv_kernel<MR, RW><<<grid, block, 0, st>>>(blocks, n, nb, x, k, y);
-    return hipGetLastError();
+    if (qtype == 14) return launch_q<14, MR, 1, MR <= 2 ? 4 : 8>(blocks, n, nb, x, k, y, st);
+    if (MR >= 3 && n >= 4096u) return launch_q<12, MR, 2, 4>(blocks, n, nb, x, k, y, st);
+    return launch_q<12, MR, 1, 4>(blocks, n, nb, x, k, y, st);
 }
 
 }  // namespace
 
-// Rows per wave: enough rows that each activation value loaded serves
-// several weights, few enough that a small n still spreads over the chip.
-int kgemv_rows_per_wave(uint32_t m, uint32_t n) {
-    (void)m;
-    return n >= 4096u ? 2 : 1;
-}
-
 hipError_t launch_kquant_gemv(int qtype, const uint8_t* blocks, uint32_t n, uint32_t k, const float* x,
                               uint32_t m, float* y, hipStream_t st) {
     const uint32_t nb = k / kQK;
-    const int rw = kgemv_rows_per_wave(m, n);
-#define RZ_KGEMV_CASE(MR)                                                                     \
-    case MR:                                                                                  \
-        return rw == 2 ? launch_mr<MR, 2>(qtype, blocks, n, nb, x, k, y, st)                  \
-                       : launch_mr<MR, 1>(qtype, blocks, n, nb, x, k, y, st);
+#define RZ_KGEMV_CASE(MR) \
+    case MR:              \
+        return launch_mr<MR>(qtype, blocks, n, nb, x, k, y, st);
     switch (m) {
         RZ_KGEMV_CASE(1)
         RZ_KGEMV_CASE(2)

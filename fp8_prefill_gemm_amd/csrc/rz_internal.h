@@ -38,6 +38,5 @@ hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hi
 // y[m][n] = x[m][k] * dequant(blocks)^T for 1 <= m <= RZ_KGEMV_MAX_M.
 hipError_t launch_kquant_gemv(int qtype, const uint8_t* blocks, uint32_t n, uint32_t k, const float* x,
                               uint32_t m, float* y, hipStream_t st);
-int kgemv_rows_per_wave(uint32_t m, uint32_t n);
 
 }  // namespace rz
