@@ -40,6 +40,7 @@ _SIGS = {
     "rz_pad_m": (_u32, [_u32]),
     "rz_workspace_bytes": (ctypes.c_size_t, []),
     "rz_fp8_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
+    "rz_fp8_pack_weights": (_i32, [_u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "rz_fp8_quant_act": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp, _vp]),
     "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
@@ -148,6 +149,35 @@ def rz_fp8_pack_weight(qtype: int, blocks, n: int, k: int, w_fp8=None, ws=None, 
     _check(lib().rz_fp8_pack_weight(qtype, _ptr(blocks), n, k, _ptr(w_fp8), ctypes.addressof(scale),
                                     ctypes.addressof(amax), _ptr(ws), _stream(stream, dev)))
     return w_fp8, scale.value, amax.value
+
+
+def rz_fp8_pack_weights(weights, ws=None, stream=None):
+    """weights: sequence of (qtype, blocks, n, k, w_fp8 or None) -> list of
+    (w_fp8, w_scale, w_absmax), packed in one call with one host wait."""
+    torch = _torch()
+    weights = list(weights)
+    cnt = len(weights)
+    if cnt == 0:
+        return []
+    dev = weights[0][1].device
+    outs = []
+    for q, b, n, k, w8 in weights:
+        _require_cuda(b, w8)
+        outs.append(torch.empty((n, k), dtype=torch.uint8, device=b.device) if w8 is None else w8)
+    if ws is None:
+        ws = workspace(dev)
+    _require_cuda(ws)
+    qt = (ctypes.c_int * cnt)(*[w[0] for w in weights])
+    bp = (ctypes.c_void_p * cnt)(*[_ptr(w[1]) for w in weights])
+    nn = (ctypes.c_uint32 * cnt)(*[w[2] for w in weights])
+    kk = (ctypes.c_uint32 * cnt)(*[w[3] for w in weights])
+    op = (ctypes.c_void_p * cnt)(*[_ptr(o) for o in outs])
+    sc = (ctypes.c_float * cnt)()
+    am = (ctypes.c_float * cnt)()
+    _check(lib().rz_fp8_pack_weights(cnt, ctypes.addressof(qt), ctypes.addressof(bp), ctypes.addressof(nn),
+                                     ctypes.addressof(kk), ctypes.addressof(op), ctypes.addressof(sc),
+                                     ctypes.addressof(am), _ptr(ws), _stream(stream, dev)))
+    return [(outs[i], sc[i], am[i]) for i in range(cnt)]
 
 
 def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):

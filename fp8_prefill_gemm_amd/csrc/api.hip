@@ -197,6 +197,96 @@ int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, ui
     return RZ_OK;
 }
 
+// Per-thread array of `count` four-float slots of coherent pinned host memory
+// for rz_fp8_pack_weights (grown on demand, kept until the process ends);
+// null if the allocation fails.
+static float* host_scale_slots(uint32_t count) {
+    thread_local float* slots = nullptr;
+    thread_local uint32_t cap = 0;
+    if (count > cap) {
+        uint32_t want = cap ? cap : 256u;
+        while (want < count) want *= 2u;
+        void* p = nullptr;
+        if (hipHostMalloc(&p, (size_t)want * 4 * sizeof(float), hipHostMallocCoherent | hipHostMallocPortable) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || dp != p) {
+            (void)hipGetLastError();
+            (void)hipHostFree(p);
+            return nullptr;
+        }
+        if (slots) (void)hipHostFree(slots);  // no kernel of this thread still writes the old array
+        slots = static_cast<float*>(p);
+        cap = want;
+    }
+    return slots;
+}
+
+int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* blocks, const uint32_t* n,
+                        const uint32_t* k, uint8_t* const* w_fp8, float* w_scale_host, float* w_absmax_host,
+                        void* ws, void* stream) {
+    static const char* fn = "rz_fp8_pack_weights";
+    if (count == 0) return RZ_OK;
+    if (!qtypes || !blocks || !n || !k || !w_fp8 || !w_scale_host || !ws)
+        return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (count > (1u << 24)) return fail(RZ_ERR_SHAPE, "%s: count=%u too large", fn, count);
+    for (uint32_t i = 0; i < count; ++i) {
+        if (!blocks[i] || !w_fp8[i]) return fail(RZ_ERR_NULL, "%s: weight %u: null pointer", fn, i);
+        if (!qtype_ok(qtypes[i])) return fail(RZ_ERR_QTYPE, "%s: weight %u: unsupported qtype %d", fn, i, qtypes[i]);
+        if (k[i] == 0 || k[i] % 256u != 0)
+            return fail(RZ_ERR_SHAPE, "%s: weight %u: k=%u must be a positive multiple of 256", fn, i, k[i]);
+        if (n[i] == 0) return fail(RZ_ERR_SHAPE, "%s: weight %u: n must be positive", fn, i);
+        if ((uint64_t)n[i] * k[i] > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: weight %u: n*k too large", fn, i);
+        if (!aligned16(blocks[i]) || !aligned16(w_fp8[i]))
+            return fail(RZ_ERR_ALIGN, "%s: weight %u: device pointers must be 16-byte aligned", fn, i);
+    }
+    if (!aligned16(ws)) return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    float* slots = host_scale_slots(count);
+    if (!slots) {  // no pinned slots: one weight at a time, each with its own wait
+        for (uint32_t i = 0; i < count; ++i) {
+            const int r = rz_fp8_pack_weight(qtypes[i], blocks[i], n[i], k[i], w_fp8[i], w_scale_host + i,
+                                             w_absmax_host ? w_absmax_host + i : nullptr, ws, stream);
+            if (r != RZ_OK) return r;
+        }
+        return RZ_OK;
+    }
+    hipStream_t st = as_stream(stream);
+    thread_local uint32_t last_ticket = 0x80000000u;  // apart from rz_fp8_pack_weight's tickets
+    uint32_t first = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint32_t ticket = ++last_ticket == 0 ? ++last_ticket : last_ticket;  // never 0
+        if (i == 0) first = ticket;
+        reinterpret_cast<volatile uint32_t*>(slots + 4 * i)[3] = 0;  // not yet this call's ticket
+        const hipError_t e = rz::launch_pack(qtypes[i], static_cast<const uint8_t*>(blocks[i]),
+                                             (uint64_t)n[i] * (k[i] / 256u), w_fp8[i], static_cast<uint8_t*>(ws),
+                                             slots + 4 * i, ticket, st);
+        if (e != hipSuccess) {
+            // the weights before i are enqueued: wait for their scales so no kernel still
+            // writes the slots, then report the failure
+            for (uint32_t j = 0; j < i; ++j) {
+                uint32_t t = first + j;
+                if (t < first) ++t;  // the ticket sequence skipped 0
+                (void)wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * j) + 3, t, st);
+            }
+            return hip_fail(e, fn);
+        }
+    }
+    uint32_t t = first;
+    for (uint32_t i = 0; i < count; ++i, ++t) {
+        if (t == 0) ++t;
+        const hipError_t e = wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * i) + 3, t, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        const volatile float* v = slots + 4 * i;  // written by the device before the ticket
+        w_scale_host[i] = v[2];
+        if (w_absmax_host) w_absmax_host[i] = v[0];
+    }
+    return RZ_OK;
+}
+
 int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, float* act_scale_dev,
                      void* ws, void* stream) {
     static const char* fn = "rz_fp8_quant_act";

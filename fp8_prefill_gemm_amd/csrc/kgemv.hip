@@ -40,25 +40,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// 16 bytes at a 2-byte-aligned address p: one 16-byte load at p rounded down
-// to 4 bytes plus one more word, recombined with byte funnel shifts.  Every
-// byte read lies in [p - 2, p + 18): the caller guarantees p + 18 stays
-// inside the buffer when p is not 4-byte aligned (the extra word is then
-// needed); when p is, the extra word read is the load's own last word.
-__device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
-    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 2u);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(p - sh);  // keeps the global address space
-    uint32_t v[4];
-    __builtin_memcpy(v, w, 16);  // dword-aligned 16-byte load
-    const uint32_t e = w[sh ? 4 : 3];
-    uint4 r;
-    r.x = __builtin_amdgcn_alignbyte(v[1], v[0], sh);
-    r.y = __builtin_amdgcn_alignbyte(v[2], v[1], sh);
-    r.z = __builtin_amdgcn_alignbyte(v[3], v[2], sh);
-    r.w = __builtin_amdgcn_alignbyte(e, v[3], sh);
-    return r;
-}
-
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -17,9 +17,11 @@
 // Thread mapping.  Q4_K: a super-block is 8 units of 16 quant bytes; 8
 // consecutive lanes take one block (its 16-byte header plus one 16-byte
 // quant slice each), so a wave reads 8 whole consecutive blocks and writes
-// their 2 KB of output.  Q6_K: 210-byte blocks are not 16-byte aligned, so a
-// workgroup stages 64 consecutive blocks (13440 bytes, 16-byte aligned) into
-// LDS with a 224-byte stride, then 4 lanes take one block.
+// their 2 KB of output.  Q6_K: 4 consecutive lanes take one block (a half
+// and a 16-element offset each), so a wave reads 16 consecutive blocks;
+// 210-byte blocks start 2-byte aligned, and each 16-byte field is read with
+// a 4-byte-aligned load plus byte funnel shifts.  Each thread issues the
+// loads of several units before it decodes the first.
 #include "rz_device.h"
 #include "rz_internal.h"
 
@@ -27,45 +29,52 @@ namespace rz {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQ6Chunk = 64;  // Q6_K blocks staged per workgroup iteration
+// Q4_K units (32 weights) per thread and loop iteration in the two pack
+// passes; Q6_K takes half as many of its 64-weight units.
+constexpr int kAbsmaxUnits = 4;
+constexpr int kEncodeUnits = 2;
 
-// Calls unit(...) for every decode unit of the tensor, in an order that keeps
-// each wave on contiguous memory:
-//   Q4_K: unit(b, s, head, qs) for block b and 16-byte quant slice s;
-//   Q6_K: unit(b, h, l0, ql_a, ql_b, qh, sc4, dbits) (see q6k_load_unit).
-template <int QT, typename F>
-__device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, uint64_t nb, uint8_t* lds,
-                                            F&& unit) {
-    if constexpr (QT == 12) {
-        // two units per iteration (g and g + stride), loads issued first
-        const uint64_t units = nb * 8;
-        const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-        for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < units; g += 2 * stride) {
-            const uint64_t g2 = g + stride;
-            const bool two = g2 < units;
-            const uint8_t* bp = blocks + (g >> 3) * kQ4Bytes;
-            const uint8_t* bp2 = blocks + ((two ? g2 : g) >> 3) * kQ4Bytes;
-            const uint4 head = *reinterpret_cast<const uint4*>(bp);
-            const uint4 qs = *reinterpret_cast<const uint4*>(bp + 16 + 16 * (int)(g & 7));
-            const uint4 head2 = *reinterpret_cast<const uint4*>(bp2);
-            const uint4 qs2 = *reinterpret_cast<const uint4*>(bp2 + 16 + 16 * (int)(g2 & 7));
-            unit(g >> 3, (int)(g & 7), head, qs);
-            if (two) unit(g2 >> 3, (int)(g2 & 7), head2, qs2);
-        }
-    } else {
-        const uint64_t nchunks = (nb + kQ6Chunk - 1) / kQ6Chunk;
-        for (uint64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
-            const uint64_t b0 = ch * kQ6Chunk;
-            const int nbc = (int)((nb - b0) < (uint64_t)kQ6Chunk ? (nb - b0) : kQ6Chunk);
-            q6k_stage<kThreads>(blocks + b0 * kQ6Bytes, nbc, lds);
-            for (int t = threadIdx.x; t < nbc * 4; t += kThreads) {
-                const int bl = t >> 2, h = (t >> 1) & 1, l0 = (t & 1) * 16;
-                uint4 ql_a, ql_b, qh;
-                uint32_t sc4, dbits;
-                q6k_load_unit(lds, bl, h, l0, ql_a, ql_b, qh, sc4, dbits);
-                unit(b0 + bl, h, l0, ql_a, ql_b, qh, sc4, dbits);
+// Calls unit(...) for every decode unit of the tensor, U units per thread
+// and iteration (unit g, g + stride, ...; all their loads are issued before
+// the first is used), so that each wave stays on contiguous memory:
+//   Q4_K: unit(b, s, head, qs) for block b and 16-byte quant slice s (8
+//         lanes per block);
+//   Q6_K: unit(b, h, l0, ql_a, ql_b, qh, sc4, dbits) for half h and l0 in
+//         {0, 16} of block b (4 lanes per block; see q6k_load_unit).
+template <int QT, int U, typename F>
+__device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, uint64_t nb, F&& unit) {
+    constexpr int kPer = QT == 12 ? 8 : 4;  // units per block
+    const uint64_t units = nb * kPer;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    for (uint64_t g0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g0 < units; g0 += U * stride) {
+        if constexpr (QT == 12) {
+            uint4 head[U], qs[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const uint64_t g = (g0 + i * stride < units) ? g0 + i * stride : g0;
+                const uint8_t* bp = blocks + (g >> 3) * kQ4Bytes;
+                head[i] = *reinterpret_cast<const uint4*>(bp);
+                qs[i] = *reinterpret_cast<const uint4*>(bp + 16 + 16 * (int)(g & 7));
             }
-            __syncthreads();  // LDS is restaged by the next iteration
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const uint64_t g = g0 + i * stride;
+                if (g < units) unit(g >> 3, (int)(g & 7), head[i], qs[i]);
+            }
+        } else {
+            uint4 ql_a[U], ql_b[U], qh[U];
+            uint32_t sc4[U], dbits[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const uint64_t g = (g0 + i * stride < units) ? g0 + i * stride : g0;
+                q6k_load_unit(blocks + (g >> 2) * kQ6Bytes, (int)(g >> 1) & 1, (int)(g & 1) * 16, ql_a[i], ql_b[i],
+                              qh[i], sc4[i], dbits[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const uint64_t g = g0 + i * stride;
+                if (g < units) unit(g >> 2, (int)(g >> 1) & 1, (int)(g & 1) * 16, ql_a[i], ql_b[i], qh[i], sc4[i], dbits[i]);
+            }
         }
     }
 }
@@ -73,9 +82,9 @@ __device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, 
 // Calls f(first_element, vals[16]) for every run of 16 consecutive decoded
 // weights of the tensor.
 template <int QT, typename F>
-__device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, uint64_t nb, uint8_t* lds, F&& f) {
+__device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, uint64_t nb, F&& f) {
     if constexpr (QT == 12) {
-        visit_units<12>(blocks, nb, lds, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+        visit_units<12, 2>(blocks, nb, [&](uint64_t b, int s, uint4 head, uint4 qs) {
             Q4Unit u;
             q4k_decode_unit(head, qs, s, u);
             const uint64_t base = b * kQK + 64 * (s >> 1) + 16 * (s & 1);
@@ -83,7 +92,7 @@ __device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, u
             f(base + 32, u.hi);
         });
     } else {
-        visit_units<14>(blocks, nb, lds,
+        visit_units<14, 1>(blocks, nb,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             Q6Unit u;
                             q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
@@ -98,8 +107,7 @@ template <int QT>
 __global__ __launch_bounds__(kThreads) void dequant_f32_kernel(const uint8_t* __restrict__ blocks,
                                                                uint64_t nb,
                                                                float* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
-    visit_runs<QT>(blocks, nb, lds, [&](uint64_t base, const float* v) {
+    visit_runs<QT>(blocks, nb, [&](uint64_t base, const float* v) {
         float4* o = reinterpret_cast<float4*>(out + base);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -111,16 +119,15 @@ template <int QT>
 __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(const uint8_t* __restrict__ blocks,
                                                                uint64_t nb,
                                                                uint32_t* __restrict__ partial) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
     __shared__ uint32_t red[kThreads / kWave];
     uint32_t key = 0;
     if constexpr (QT == 12) {
-        visit_units<12>(blocks, nb, lds, [&](uint64_t, int s, uint4 head, uint4 qs) {
+        visit_units<12, kAbsmaxUnits>(blocks, nb, [&](uint64_t, int s, uint4 head, uint4 qs) {
             const uint32_t k = q4k_unit_key(head, qs, s);
             key = key > k ? key : k;
         });
     } else {
-        visit_units<14>(blocks, nb, lds,
+        visit_units<14, kAbsmaxUnits / 2>(blocks, nb,
                         [&](uint64_t, int, int, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             const uint32_t k = q6k_unit_key(ql_a, ql_b, qh, sc4, dbits);
                             key = key > k ? key : k;
@@ -143,7 +150,6 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
                                                                uint8_t* __restrict__ w_fp8,
                                                                float* __restrict__ scale_out,
                                                                float* __restrict__ host_out, uint32_t ticket) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[QT == 14 ? kQ6Chunk * kQ6LdsStride : 16];
     __shared__ uint32_t red[kThreads / kWave];
     const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
     // takes the short encoder when all its lanes qualify.
     const bool tensor_finite = sc.a <= 3.402823466e38f;
     if constexpr (QT == 12) {
-        visit_units<12>(blocks, nb, lds, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+        visit_units<12, kEncodeUnits>(blocks, nb, [&](uint64_t b, int s, uint4 head, uint4 qs) {
             Q4Unit u;
             q4k_decode_unit(head, qs, s, u);
             uint8_t* o = w_fp8 + b * kQK + 64 * (s >> 1) + 16 * (s & 1);
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
             }
         });
     } else {
-        visit_units<14>(blocks, nb, lds,
+        visit_units<14, kEncodeUnits / 2>(blocks, nb,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             Q6Unit u;
                             uint8_t* o = w_fp8 + b * kQK + 128 * h + l0;
@@ -198,9 +204,12 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
     }
 }
 
-// Workgroups that cover the tensor once (one pass of the visit loop).
-uint64_t groups_for(int qtype, uint64_t nb) {
-    return qtype == 12 ? (nb * 8 + kThreads - 1) / kThreads : (nb + kQ6Chunk - 1) / kQ6Chunk;
+// Workgroups that give every thread `per` units of a Q4_K tensor (`per` / 2
+// of a Q6_K one).
+uint64_t groups_for(int qtype, uint64_t nb, int per) {
+    const uint64_t units = qtype == 12 ? nb * 8 : nb * 4;
+    const uint64_t per_thread = qtype == 12 ? per : (per + 1) / 2;
+    return (units + kThreads * per_thread - 1) / (kThreads * per_thread);
 }
 
 int clamp_groups(uint64_t g, int cap) {
@@ -212,7 +221,7 @@ int clamp_groups(uint64_t g, int cap) {
 
 hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nb, float* out,
                               hipStream_t st) {
-    const int grid = clamp_groups(groups_for(qtype, nb), 1 << 16);
+    const int grid = clamp_groups(groups_for(qtype, nb, 2), 1 << 16);
     if (qtype == 12)
         dequant_f32_kernel<12><<<grid, kThreads, 0, st>>>(blocks, nb, out);
     else
@@ -224,8 +233,9 @@ hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint8_t* w
                        float* host_scale, uint32_t ticket, hipStream_t st) {
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
-    const int g1 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
-    const int g2 = clamp_groups(groups_for(qtype, nb), kMaxPartials);
+    const int g1 = clamp_groups(groups_for(qtype, nb, kAbsmaxUnits), kMaxPartials);
+    // every encode workgroup re-reduces the partial keys: keep their number bounded
+    const int g2 = clamp_groups(groups_for(qtype, nb, kEncodeUnits), kMaxPartials);
     if (qtype == 12) {
         pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
         pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale, ticket);

@@ -16,7 +16,6 @@ constexpr int kWave = 64;
 constexpr int kQK = 256;          // weights per K-quant super-block
 constexpr int kQ4Bytes = 144;     // Q4_K super-block bytes
 constexpr int kQ6Bytes = 210;     // Q6_K super-block bytes
-constexpr int kQ6LdsStride = 224; // Q6_K block stride when staged in LDS (16-aligned)
 constexpr float kFp8Max = 448.0f; // largest finite E4M3 value, code 0x7E
 
 // ---------------------------------------------------------------- E4M3
@@ -341,58 +340,37 @@ __device__ __forceinline__ uint32_t q6k_unit_key(uint4 ql_a, uint4 ql_b, uint4 q
     return key;
 }
 
-// Stage `nb` (<= 64) consecutive Q6_K blocks starting at `src` (16-byte
-// aligned: the first block of a 64-block chunk) into LDS with a 224-byte
-// stride, so that every 16-byte field of a block is 16-byte aligned in LDS.
-// The tail of the tensor is read in 2-byte pieces so nothing past the last
-// block is touched.  Must be called by all kThreads threads; ends with a
-// barrier.
-template <int kThreads>
-__device__ __forceinline__ void q6k_stage(const uint8_t* __restrict__ src, int nb, uint8_t* lds) {
-    const int bytes = nb * kQ6Bytes;
-    const int nvec = (bytes + 15) >> 4;
-    uint16_t* l16 = reinterpret_cast<uint16_t*>(lds);
-    for (int i = threadIdx.x; i < nvec; i += kThreads) {
-        const int p0 = i << 4;
-        uint32_t w[4];
-        if (p0 + 16 <= bytes) {
-            const uint4 v = *reinterpret_cast<const uint4*>(src + p0);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        } else {
-            const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src + p0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = (p0 + 4 * j < bytes) ? s16[2 * j] : 0u;
-                const uint32_t hi = (p0 + 4 * j + 2 < bytes) ? s16[2 * j + 1] : 0u;
-                w[j] = lo | (hi << 16);
-            }
-        }
-        int blk = p0 / kQ6Bytes;
-        int off = p0 - blk * kQ6Bytes;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (p0 + 2 * j < bytes) {
-                l16[(blk * kQ6LdsStride + off) >> 1] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-            }
-            off += 2;
-            if (off == kQ6Bytes) { off = 0; ++blk; }
-        }
-    }
-    __syncthreads();
+// 16 bytes at a 2-byte-aligned global address p (a field of a 210-byte
+// Q6_K block): one 16-byte load at p rounded down to 4 bytes plus one more
+// word, recombined with byte funnel shifts.  Every byte read lies in
+// [p - 2, p + 18): the caller guarantees p + 18 stays inside the buffer when
+// p is not 4-byte aligned (the extra word is then needed); when p is, the
+// extra word read is the load's own last word.
+__device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
+    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 2u);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p - sh);  // keeps the global address space
+    uint32_t v[4];
+    __builtin_memcpy(v, w, 16);  // dword-aligned 16-byte load
+    const uint32_t e = w[sh ? 4 : 3];
+    uint4 r;
+    r.x = __builtin_amdgcn_alignbyte(v[1], v[0], sh);
+    r.y = __builtin_amdgcn_alignbyte(v[2], v[1], sh);
+    r.z = __builtin_amdgcn_alignbyte(v[3], v[2], sh);
+    r.w = __builtin_amdgcn_alignbyte(e, v[3], sh);
+    return r;
 }
 
-// Read the unit (h, l0) of staged block `bl` from LDS.
-__device__ __forceinline__ void q6k_load_unit(const uint8_t* lds, int bl, int h, int l0, uint4& ql_a,
-                                              uint4& ql_b, uint4& qh, uint32_t& sc4, uint32_t& dbits) {
-    const uint8_t* b = lds + bl * kQ6LdsStride;
-    ql_a = *reinterpret_cast<const uint4*>(b + 64 * h + l0);
-    ql_b = *reinterpret_cast<const uint4*>(b + 64 * h + 32 + l0);
-    qh = *reinterpret_cast<const uint4*>(b + 128 + 32 * h + l0);
-    const uint4 sc = *reinterpret_cast<const uint4*>(b + 192);
-    const int base = 8 * h + (l0 >> 4);
-    sc4 = byte_of(sc, base) | (byte_of(sc, base + 2) << 8) | (byte_of(sc, base + 4) << 16) |
-          (byte_of(sc, base + 6) << 24);
-    dbits = *reinterpret_cast<const uint16_t*>(b + 208);
+// Load the Q6_K decode unit (half h, l0 in {0, 16}) of the block at blk
+// straight from global memory (see q6k_decode_unit).  The furthest byte
+// read is 2 past the qh run (offset <= 194), inside the block.
+__device__ __forceinline__ void q6k_load_unit(const uint8_t* blk, int h, int l0, uint4& ql_a, uint4& ql_b,
+                                              uint4& qh, uint32_t& sc4, uint32_t& dbits) {
+    ql_a = ld16_a2(blk + 64 * h + l0);
+    ql_b = ld16_a2(blk + 64 * h + 32 + l0);
+    qh = ld16_a2(blk + 128 + 32 * h + l0);
+    const uint8_t* sc = blk + 192 + 8 * h + (l0 >> 4);
+    sc4 = (uint32_t)sc[0] | ((uint32_t)sc[2] << 8) | ((uint32_t)sc[4] << 16) | ((uint32_t)sc[6] << 24);
+    dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
 }
 
 }  // namespace rz

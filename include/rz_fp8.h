@@ -101,6 +101,30 @@ int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k,
                        void* ws, void* stream);
 
 /*
+ * Pack `count` K-quant weights, each exactly as rz_fp8_pack_weight packs it,
+ * with one host wait for all their scales instead of one per weight
+ * (gemm.rs page, get_or_cache_fp8_weight, for every weight of a model: the
+ * pages pack on first use, one weight at a time).
+ *
+ *   qtypes, blocks, n, k, w_fp8   host arrays of `count` entries: weight i
+ *                 is described as the same-named arguments of
+ *                 rz_fp8_pack_weight (device pointers, caller-owned)
+ *   w_scale_host  host out, float[count]
+ *   w_absmax_host host out, float[count] (may be NULL)
+ *   ws            device workspace of rz_workspace_bytes(), reused by the
+ *                 weights in stream order
+ * Every entry is validated before anything is launched (the message names
+ * the first bad weight).  The kernels of all weights are enqueued back to
+ * back; the call returns once every scale is on the host (the codes of the
+ * last weight may still be being written, ordered before later work on
+ * `stream`).  count == 0 is a no-op.  Per-thread pinned host memory for the
+ * scales grows to the largest count seen and is kept until the process ends.
+ */
+int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* blocks,
+                        const uint32_t* n, const uint32_t* k, uint8_t* const* w_fp8,
+                        float* w_scale_host, float* w_absmax_host, void* ws, void* stream);
+
+/*
  * Quantise an fp32 activation to FP8 on the device, with no host
  * synchronisation (gemm.rs page, cublas_prefill_fp8_gemm steps 1-2; mod.rs
  * page, F32_TO_E4M3_DEVICE_SCALED_PTX).

@@ -77,6 +77,32 @@ def test_pack_validation(L):
     assert host.value == 0.0  # outputs untouched on error
 
 
+def test_pack_weights_validation(L):
+    arr = lambda ct, vals: (ct * len(vals))(*vals)
+    V = ctypes.c_void_p
+
+    def f(cnt, q, b, n, k, o, sc=True, ws=P3):
+        scale = (ctypes.c_float * max(cnt, 1))()
+        return L.rz_fp8_pack_weights(cnt, q, b, n, k, o, scale if sc else None, None, ws, None)
+    q = arr(ctypes.c_int, [12, 14])
+    b = arr(V, [P, P2])
+    n = arr(ctypes.c_uint32, [8, 4])
+    k = arr(ctypes.c_uint32, [256, 512])
+    o = arr(V, [P2, P])
+    assert f(0, None, None, None, None, None) == RZ_OK
+    assert f(2, None, b, n, k, o) == RZ_ERR_NULL
+    assert f(2, q, b, n, k, o, sc=False) == RZ_ERR_NULL
+    assert f(2, q, b, n, k, o, ws=None) == RZ_ERR_NULL
+    assert f(2, q, arr(V, [P, None]), n, k, o) == RZ_ERR_NULL
+    assert "weight 1" in _err(L)
+    assert f(2, arr(ctypes.c_int, [12, 3]), b, n, k, o) == RZ_ERR_QTYPE
+    assert f(2, q, b, n, arr(ctypes.c_uint32, [256, 300]), o) == RZ_ERR_SHAPE
+    assert f(2, q, b, arr(ctypes.c_uint32, [0, 4]), k, o) == RZ_ERR_SHAPE
+    assert "weight 0" in _err(L)
+    assert f(2, q, arr(V, [P, BAD]), n, k, o) == RZ_ERR_ALIGN
+    assert f(2, q, b, n, k, o, ws=BAD) == RZ_ERR_ALIGN
+
+
 def test_quant_act_validation(L):
     f = L.rz_fp8_quant_act
     assert f(None, 4, 256, P2, P3, P, None) == RZ_ERR_NULL

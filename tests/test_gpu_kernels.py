@@ -145,6 +145,38 @@ def test_pack_bit_exact(rz, qtype, n, k):
     np.testing.assert_array_equal(host(w8), r8)
 
 
+def test_pack_weights_batch(rz):
+    # one call, mixed formats and shapes (including an all-zero weight): every
+    # weight bit-exact against the oracle, the same as its own single call
+    specs = [(W.Q4_K, 64, 512), (W.Q6_K, 37, 1280), (W.Q4_K, 512, 3584), (W.Q6_K, 1, 256), (W.Q4_K, 3, 768)]
+    blocks = [W.weight_blocks(q, 1300 + i, n, k) for i, (q, n, k) in enumerate(specs)]
+    blocks[3][:] = 0
+    print(f"pack_weights batch of {len(specs)}", flush=True)
+    outs = rz.rz_fp8_pack_weights([(q, dev(b), n, k, None) for (q, n, k), b in zip(specs, blocks)])
+    for (q, n, k), b, (w8, scale, amax) in zip(specs, blocks, outs):
+        r8, rdq, ra = fp8_path.pack_weight(q, b, n, k)
+        assert np.float32(amax).view(np.uint32) == ra.view(np.uint32)
+        assert np.float32(scale).view(np.uint32) == rdq.view(np.uint32)
+        np.testing.assert_array_equal(host(w8), r8)
+        s8, sscale, samax = rz.rz_fp8_pack_weight(q, dev(b), n, k)
+        assert (sscale, samax) == (scale, amax)
+        np.testing.assert_array_equal(host(s8), host(w8))
+
+
+def test_pack_weights_many(rz):
+    # more weights than the first allocation of host scale slots (256), twice
+    cnt = 300
+    blocks = [W.weight_blocks(W.Q4_K if i % 3 else W.Q6_K, 1400 + i, 2, 256) for i in range(cnt)]
+    qts = [W.Q4_K if i % 3 else W.Q6_K for i in range(cnt)]
+    for rep in range(2):
+        print(f"pack_weights batch of {cnt}, pass {rep}", flush=True)
+        outs = rz.rz_fp8_pack_weights([(q, dev(b), 2, 256, None) for q, b in zip(qts, blocks)])
+        for q, b, (w8, scale, amax) in zip(qts, blocks, outs):
+            r8, rdq, ra = fp8_path.pack_weight(q, b, 2, 256)
+            assert np.float32(scale) == rdq and np.float32(amax) == ra
+            np.testing.assert_array_equal(host(w8), r8)
+
+
 def test_pack_zero_weight(rz):
     blocks = np.zeros((4 * 2, 144), np.uint8)
     w8, scale, amax = rz.rz_fp8_pack_weight(W.Q4_K, dev(blocks), 4, 512)
