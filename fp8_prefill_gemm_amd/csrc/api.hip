@@ -9,6 +9,7 @@
 
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/rz_fp8.h"
 #include "rz_internal.h"
@@ -255,30 +256,47 @@ int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* bl
         return RZ_OK;
     }
     hipStream_t st = as_stream(stream);
+    // Consecutive weights whose pass-1 workgroups fit the workspace's partial
+    // keys together share one launch per pass (a layer's small q/k/v/o
+    // weights), so their latencies overlap.
     thread_local uint32_t last_ticket = 0x80000000u;  // apart from rz_fp8_pack_weight's tickets
-    uint32_t first = 0;
-    for (uint32_t i = 0; i < count; ++i) {
-        const uint32_t ticket = ++last_ticket == 0 ? ++last_ticket : last_ticket;  // never 0
-        if (i == 0) first = ticket;
-        reinterpret_cast<volatile uint32_t*>(slots + 4 * i)[3] = 0;  // not yet this call's ticket
-        const hipError_t e = rz::launch_pack(qtypes[i], static_cast<const uint8_t*>(blocks[i]),
-                                             (uint64_t)n[i] * (k[i] / 256u), w_fp8[i], static_cast<uint8_t*>(ws),
-                                             slots + 4 * i, ticket, st);
+    std::vector<uint32_t> tickets(count);
+    for (uint32_t i = 0; i < count;) {
+        int qt[rz::kMaxPackSet];
+        const uint8_t* bl[rz::kMaxPackSet];
+        uint64_t nbv[rz::kMaxPackSet];
+        uint8_t* wo[rz::kMaxPackSet];
+        float* hs[rz::kMaxPackSet];
+        uint32_t tk[rz::kMaxPackSet];
+        int cnt = 0, groups = 0;
+        while (i + cnt < count && cnt < rz::kMaxPackSet) {
+            const uint32_t j = i + (uint32_t)cnt;
+            const uint64_t nbj = (uint64_t)n[j] * (k[j] / 256u);
+            const int gj = rz::pack_absmax_groups(qtypes[j], nbj);
+            if (cnt > 0 && groups + gj > rz::kMaxPartials) break;
+            groups += gj;
+            tickets[j] = ++last_ticket == 0 ? ++last_ticket : last_ticket;  // never 0
+            reinterpret_cast<volatile uint32_t*>(slots + 4 * j)[3] = 0;        // not yet this call's ticket
+            qt[cnt] = qtypes[j];
+            bl[cnt] = static_cast<const uint8_t*>(blocks[j]);
+            nbv[cnt] = nbj;
+            wo[cnt] = w_fp8[j];
+            hs[cnt] = slots + 4 * j;
+            tk[cnt] = tickets[j];
+            ++cnt;
+        }
+        const hipError_t e = rz::launch_pack_set(cnt, qt, bl, nbv, wo, static_cast<uint8_t*>(ws), hs, tk, st);
         if (e != hipSuccess) {
-            // the weights before i are enqueued: wait for their scales so no kernel still
-            // writes the slots, then report the failure
-            for (uint32_t j = 0; j < i; ++j) {
-                uint32_t t = first + j;
-                if (t < first) ++t;  // the ticket sequence skipped 0
-                (void)wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * j) + 3, t, st);
-            }
+            // the weights before i are enqueued: wait for their scales so that no
+            // kernel still writes the slots, then report the failure
+            for (uint32_t j = 0; j < i; ++j)
+                (void)wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * j) + 3, tickets[j], st);
             return hip_fail(e, fn);
         }
+        i += (uint32_t)cnt;
     }
-    uint32_t t = first;
-    for (uint32_t i = 0; i < count; ++i, ++t) {
-        if (t == 0) ++t;
-        const hipError_t e = wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * i) + 3, t, st);
+    for (uint32_t i = 0; i < count; ++i) {
+        const hipError_t e = wait_for_ticket(reinterpret_cast<const uint32_t*>(slots + 4 * i) + 3, tickets[i], st);
         if (e != hipSuccess) return hip_fail(e, fn);
         const volatile float* v = slots + 4 * i;  // written by the device before the ticket
         w_scale_host[i] = v[2];

@@ -41,12 +41,14 @@ constexpr int kEncodeUnits = 2;
 //         lanes per block);
 //   Q6_K: unit(b, h, l0, ql_a, ql_b, qh, sc4, dbits) for half h and l0 in
 //         {0, 16} of block b (4 lanes per block; see q6k_load_unit).
+// The tensor is shared by `ngroups` workgroups; this one is number `bid`.
 template <int QT, int U, typename F>
-__device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, uint64_t nb, F&& unit) {
+__device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, uint64_t nb, int bid, int ngroups,
+                                            F&& unit) {
     constexpr int kPer = QT == 12 ? 8 : 4;  // units per block
     const uint64_t units = nb * kPer;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t g0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g0 < units; g0 += U * stride) {
+    const uint64_t stride = (uint64_t)ngroups * kThreads;
+    for (uint64_t g0 = (uint64_t)bid * kThreads + threadIdx.x; g0 < units; g0 += U * stride) {
         if constexpr (QT == 12) {
             uint4 head[U], qs[U];
 #pragma unroll
@@ -83,8 +85,9 @@ __device__ __forceinline__ void visit_units(const uint8_t* __restrict__ blocks, 
 // weights of the tensor.
 template <int QT, typename F>
 __device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, uint64_t nb, F&& f) {
+    const int bid = blockIdx.x, ngroups = gridDim.x;
     if constexpr (QT == 12) {
-        visit_units<12, 2>(blocks, nb, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+        visit_units<12, 2>(blocks, nb, bid, ngroups, [&](uint64_t b, int s, uint4 head, uint4 qs) {
             Q4Unit u;
             q4k_decode_unit(head, qs, s, u);
             const uint64_t base = b * kQK + 64 * (s >> 1) + 16 * (s & 1);
@@ -92,7 +95,7 @@ __device__ __forceinline__ void visit_runs(const uint8_t* __restrict__ blocks, u
             f(base + 32, u.hi);
         });
     } else {
-        visit_units<14, 1>(blocks, nb,
+        visit_units<14, 1>(blocks, nb, bid, ngroups,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             Q6Unit u;
                             q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
@@ -114,64 +117,36 @@ __global__ __launch_bounds__(kThreads) void dequant_f32_kernel(const uint8_t* __
     });
 }
 
-// Pass 1: one absmax key per workgroup (from each unit's extreme quants).
+// Pass 1 of one weight: this workgroup's absmax key (from each unit's
+// extreme quants), reduced over the workgroup.
 template <int QT>
-__global__ __launch_bounds__(kThreads) void pack_absmax_kernel(const uint8_t* __restrict__ blocks,
-                                                               uint64_t nb,
-                                                               uint32_t* __restrict__ partial) {
-    __shared__ uint32_t red[kThreads / kWave];
+__device__ __forceinline__ uint32_t absmax_part(const uint8_t* __restrict__ blocks, uint64_t nb, int bid, int ngroups,
+                                                uint32_t* red) {
     uint32_t key = 0;
     if constexpr (QT == 12) {
-        visit_units<12, kAbsmaxUnits>(blocks, nb, [&](uint64_t, int s, uint4 head, uint4 qs) {
+        visit_units<12, kAbsmaxUnits>(blocks, nb, bid, ngroups, [&](uint64_t, int s, uint4 head, uint4 qs) {
             const uint32_t k = q4k_unit_key(head, qs, s);
             key = key > k ? key : k;
         });
     } else {
-        visit_units<14, kAbsmaxUnits / 2>(blocks, nb,
+        visit_units<14, kAbsmaxUnits / 2>(blocks, nb, bid, ngroups,
                         [&](uint64_t, int, int, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             const uint32_t k = q6k_unit_key(ql_a, ql_b, qh, sc4, dbits);
                             key = key > k ? key : k;
                         });
     }
-    key = block_max_u32<kThreads>(key, red);
-    if (threadIdx.x == 0) partial[blockIdx.x] = key;
+    return block_max_u32<kThreads>(key, red);
 }
 
-// Pass 2: reduce the pass-1 keys, derive the scales, encode.  Workgroup 0
-// publishes {a, q, dq, 0} to scale_out and, when given, {a, q, dq} to
-// host_out (coherent host memory) followed by `ticket` in its fourth word,
-// stored with release order at system scope: a host thread that sees the
-// ticket there can read the scales while the codes are still being written.
+// Pass 2 of one weight: re-decode this workgroup's units and encode them
+// with the scale q.  With a finite absmax and a unit whose f16 scales are
+// finite, every product is finite and at most 448(1 + 2^-23) in magnitude:
+// the wave takes the short encoder when all its lanes qualify.
 template <int QT>
-__global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __restrict__ blocks,
-                                                               uint64_t nb,
-                                                               const uint32_t* __restrict__ partial,
-                                                               int npartial,
-                                                               uint8_t* __restrict__ w_fp8,
-                                                               float* __restrict__ scale_out,
-                                                               float* __restrict__ host_out, uint32_t ticket) {
-    __shared__ uint32_t red[kThreads / kWave];
-    const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        scale_out[0] = sc.a;
-        scale_out[1] = sc.q;
-        scale_out[2] = sc.dq;
-        scale_out[3] = 0.0f;
-        if (host_out) {
-            host_out[0] = sc.a;
-            host_out[1] = sc.q;
-            host_out[2] = sc.dq;
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(host_out) + 3, ticket, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-    }
-    const float q = sc.q;
-    // With a finite absmax and a unit whose f16 scales are finite, every
-    // product is finite and at most 448(1 + 2^-23) in magnitude: the wave
-    // takes the short encoder when all its lanes qualify.
-    const bool tensor_finite = sc.a <= 3.402823466e38f;
+__device__ __forceinline__ void encode_part(const uint8_t* __restrict__ blocks, uint64_t nb, int bid, int ngroups,
+                                            uint8_t* __restrict__ w_fp8, float q, bool tensor_finite) {
     if constexpr (QT == 12) {
-        visit_units<12, kEncodeUnits>(blocks, nb, [&](uint64_t b, int s, uint4 head, uint4 qs) {
+        visit_units<12, kEncodeUnits>(blocks, nb, bid, ngroups, [&](uint64_t b, int s, uint4 head, uint4 qs) {
             Q4Unit u;
             q4k_decode_unit(head, qs, s, u);
             uint8_t* o = w_fp8 + b * kQK + 64 * (s >> 1) + 16 * (s & 1);
@@ -185,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
             }
         });
     } else {
-        visit_units<14, kEncodeUnits / 2>(blocks, nb,
+        visit_units<14, kEncodeUnits / 2>(blocks, nb, bid, ngroups,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
                             Q6Unit u;
                             uint8_t* o = w_fp8 + b * kQK + 128 * h + l0;
@@ -202,6 +177,68 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(const uint8_t* __
                             }
                         });
     }
+}
+
+// The weight of set P that workgroup b of a launch belongs to (`start` holds
+// the first workgroup of each weight and, at [count], the grid size).
+__device__ __forceinline__ int set_member(const int* start, int count, int b) {
+    int i = 0;
+    while (i + 1 < count && b >= start[i + 1]) ++i;
+    return i;
+}
+
+// Pass 1 over a set of weights: weight i owns workgroups [g1[i], g1[i+1]),
+// and each writes its key to partial[blockIdx.x].  QT = 12 / 14 when every
+// weight of the set has that type, 0 for a mixed set (the type is then read
+// per weight; it is uniform over a workgroup).
+template <int QT>
+__global__ __launch_bounds__(kThreads) void pack_absmax_kernel(PackSet P, uint32_t* __restrict__ partial) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const int i = set_member(P.g1, P.count, blockIdx.x);
+    const int bid = blockIdx.x - P.g1[i], ng = P.g1[i + 1] - P.g1[i];
+    const int qt = QT ? QT : P.qtype[i];
+    uint32_t key;
+    if (qt == 12)
+        key = absmax_part<12>(P.blocks[i], P.nb[i], bid, ng, red);
+    else
+        key = absmax_part<14>(P.blocks[i], P.nb[i], bid, ng, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = key;
+}
+
+// Pass 2 over a set of weights: weight i owns workgroups [g2[i], g2[i+1]).
+// Each workgroup reduces its weight's pass-1 keys, derives the scales and
+// encodes.  The first workgroup of weight i publishes {a, q, dq, 0} to
+// scale_out[4i..] and, when host[i] is given, {a, q, dq} to that coherent
+// host memory followed by ticket[i] in its fourth word, stored with release
+// order at system scope: a host thread that sees the ticket there can read
+// the scales while the codes are still being written.
+template <int QT>
+__global__ __launch_bounds__(kThreads) void pack_encode_kernel(PackSet P, const uint32_t* __restrict__ partial,
+                                                               float* __restrict__ scale_out) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const int i = set_member(P.g2, P.count, blockIdx.x);
+    const int bid = blockIdx.x - P.g2[i], ng = P.g2[i + 1] - P.g2[i];
+    const Scales sc = scales_from_key(reduce_partials<kThreads>(partial + P.g1[i], P.g1[i + 1] - P.g1[i], red));
+    if (bid == 0 && threadIdx.x == 0) {
+        float* so = scale_out + 4 * i;
+        so[0] = sc.a;
+        so[1] = sc.q;
+        so[2] = sc.dq;
+        so[3] = 0.0f;
+        if (float* ho = P.host[i]) {
+            ho[0] = sc.a;
+            ho[1] = sc.q;
+            ho[2] = sc.dq;
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(ho) + 3, P.ticket[i], __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+    const bool tensor_finite = sc.a <= 3.402823466e38f;
+    const int qt = QT ? QT : P.qtype[i];
+    if (qt == 12)
+        encode_part<12>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], sc.q, tensor_finite);
+    else
+        encode_part<14>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], sc.q, tensor_finite);
 }
 
 // Workgroups that give every thread `per` units of a Q4_K tensor (`per` / 2
@@ -229,21 +266,49 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nb, flo
     return hipGetLastError();
 }
 
-hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint8_t* w_fp8, uint8_t* ws,
-                       float* host_scale, uint32_t ticket, hipStream_t st) {
+int pack_absmax_groups(int qtype, uint64_t nb) {
+    return clamp_groups(groups_for(qtype, nb, kAbsmaxUnits), kMaxPartials);
+}
+
+hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* blocks, const uint64_t* nb,
+                           uint8_t* const* w_fp8, uint8_t* ws, float* const* host_scale, const uint32_t* ticket,
+                           hipStream_t st) {
+    if (count < 1 || count > kMaxPackSet) return hipErrorInvalidValue;
+    PackSet P{};
+    P.count = count;
+    bool same = true;
+    for (int i = 0; i < count; ++i) {
+        P.qtype[i] = qtype[i];
+        P.blocks[i] = blocks[i];
+        P.nb[i] = nb[i];
+        P.w_fp8[i] = w_fp8[i];
+        P.host[i] = host_scale ? host_scale[i] : nullptr;
+        P.ticket[i] = ticket ? ticket[i] : 0u;
+        P.g1[i + 1] = P.g1[i] + pack_absmax_groups(qtype[i], nb[i]);
+        // every encode workgroup re-reduces its weight's keys: keep their number bounded
+        P.g2[i + 1] = P.g2[i] + clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials);
+        same = same && qtype[i] == qtype[0];
+    }
+    if (P.g1[count] > kMaxPartials) return hipErrorInvalidValue;
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
-    const int g1 = clamp_groups(groups_for(qtype, nb, kAbsmaxUnits), kMaxPartials);
-    // every encode workgroup re-reduces the partial keys: keep their number bounded
-    const int g2 = clamp_groups(groups_for(qtype, nb, kEncodeUnits), kMaxPartials);
-    if (qtype == 12) {
-        pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale, ticket);
+    const int g1 = P.g1[count], g2 = P.g2[count];
+    if (same && qtype[0] == 12) {
+        pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(P, partial);
+        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
+    } else if (same) {
+        pack_absmax_kernel<14><<<g1, kThreads, 0, st>>>(P, partial);
+        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
     } else {
-        pack_absmax_kernel<14><<<g1, kThreads, 0, st>>>(blocks, nb, partial);
-        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(blocks, nb, partial, g1, w_fp8, scale_out, host_scale, ticket);
+        pack_absmax_kernel<0><<<g1, kThreads, 0, st>>>(P, partial);
+        pack_encode_kernel<0><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint8_t* w_fp8, uint8_t* ws,
+                       float* host_scale, uint32_t ticket, hipStream_t st) {
+    return launch_pack_set(1, &qtype, &blocks, &nb, &w_fp8, ws, &host_scale, &ticket, st);
 }
 
 }  // namespace rz

@@ -11,10 +11,27 @@
 namespace rz {
 
 // Workspace layout (bytes): [0, 8192) partial absmax keys (uint32, at most
-// kMaxPartials), [8192, 8208) the weight path's {a, q, dq, 0}.
+// kMaxPartials), [8192, 8448) the weight path's {a, q, dq, 0}, one record per
+// weight of a pack set (room for 16).
 constexpr int kMaxPartials = 2048;
 constexpr size_t kWsScaleOffset = 8192;
 constexpr size_t kWsBytes = 8448;
+
+// A set of weights packed by one pass-1 and one pass-2 launch (kquant.hip):
+// weight i owns pass-1 workgroups [g1[i], g1[i+1]) (and their partial keys)
+// and pass-2 workgroups [g2[i], g2[i+1]); g1[count] <= kMaxPartials.
+constexpr int kMaxPackSet = 8;
+struct PackSet {
+    int count;
+    int qtype[kMaxPackSet];
+    const uint8_t* blocks[kMaxPackSet];
+    uint64_t nb[kMaxPackSet];
+    uint8_t* w_fp8[kMaxPackSet];
+    float* host[kMaxPackSet];
+    uint32_t ticket[kMaxPackSet];
+    int g1[kMaxPackSet + 1];
+    int g2[kMaxPackSet + 1];
+};
 
 // ---- kquant.hip
 hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nblocks, float* out,
@@ -25,6 +42,15 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nblocks
 // uint32, release order) in its fourth word, before the codes.
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nblocks, uint8_t* w_fp8,
                        uint8_t* ws, float* host_scale, uint32_t ticket, hipStream_t st);
+// Pass-1 workgroups (= partial keys) of one weight.
+int pack_absmax_groups(int qtype, uint64_t nb);
+// The two passes for `count` (<= kMaxPackSet) weights whose pass-1 groups
+// add up to at most kMaxPartials; weight i's scales go to ws +
+// kWsScaleOffset + 16 i and, when host_scale[i] is not null, to that host
+// memory followed by ticket[i].
+hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* blocks, const uint64_t* nb,
+                           uint8_t* const* w_fp8, uint8_t* ws, float* const* host_scale, const uint32_t* ticket,
+                           hipStream_t st);
 
 // ---- actquant.hip
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,

@@ -163,6 +163,20 @@ def test_pack_weights_batch(rz):
         np.testing.assert_array_equal(host(s8), host(w8))
 
 
+def test_pack_weights_sets_split_by_partial_keys(rz):
+    # 10752x3584 Q4_K weights take 1176 pass-1 workgroups each and the Q6_K one
+    # 588: the first two share a launch, the third needs its own (the partial
+    # keys of one launch are capped at 2048)
+    specs = [(W.Q4_K, 10752, 3584), (W.Q6_K, 5376, 3584), (W.Q4_K, 10752, 3584)]
+    blocks = [W.weight_blocks(q, 1500 + i, n, k) for i, (q, n, k) in enumerate(specs)]
+    print("pack_weights: three large weights in two launch sets", flush=True)
+    outs = rz.rz_fp8_pack_weights([(q, dev(b), n, k, None) for (q, n, k), b in zip(specs, blocks)])
+    for (q, n, k), b, (w8, scale, amax) in zip(specs, blocks, outs):
+        r8, rdq, ra = fp8_path.pack_weight(q, b, n, k)
+        assert np.float32(scale) == rdq and np.float32(amax) == ra
+        np.testing.assert_array_equal(host(w8), r8)
+
+
 def test_pack_weights_many(rz):
     # more weights than the first allocation of host scale slots (256), twice
     cnt = 300
