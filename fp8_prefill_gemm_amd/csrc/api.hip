@@ -257,8 +257,8 @@ int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* bl
     }
     hipStream_t st = as_stream(stream);
     // Consecutive weights whose pass-1 workgroups fit the workspace's partial
-    // keys together share one launch per pass (a layer's small q/k/v/o
-    // weights), so their latencies overlap.
+    // keys together (up to 8 weights) share one launch per pass: a whole
+    // layer of the 7B-class model, so the kernels' latencies and tails overlap.
     thread_local uint32_t last_ticket = 0x80000000u;  // apart from rz_fp8_pack_weight's tickets
     std::vector<uint32_t> tickets(count);
     for (uint32_t i = 0; i < count;) {
@@ -273,7 +273,7 @@ int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* bl
             const uint32_t j = i + (uint32_t)cnt;
             const uint64_t nbj = (uint64_t)n[j] * (k[j] / 256u);
             const int gj = rz::pack_absmax_groups(qtypes[j], nbj);
-            if (cnt > 0 && groups + gj > rz::kMaxPartials) break;
+            if (cnt > 0 && groups + gj > rz::kWsPartials) break;
             groups += gj;
             tickets[j] = ++last_ticket == 0 ? ++last_ticket : last_ticket;  // never 0
             reinterpret_cast<volatile uint32_t*>(slots + 4 * j)[3] = 0;        // not yet this call's ticket

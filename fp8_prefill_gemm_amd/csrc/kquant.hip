@@ -289,7 +289,7 @@ hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* bl
         P.g2[i + 1] = P.g2[i] + clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials);
         same = same && qtype[i] == qtype[0];
     }
-    if (P.g1[count] > kMaxPartials) return hipErrorInvalidValue;
+    if (P.g1[count] > kWsPartials) return hipErrorInvalidValue;
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
     const int g1 = P.g1[count], g2 = P.g2[count];

@@ -10,16 +10,19 @@
 
 namespace rz {
 
-// Workspace layout (bytes): [0, 8192) partial absmax keys (uint32, at most
-// kMaxPartials), [8192, 8448) the weight path's {a, q, dq, 0}, one record per
+// Workspace layout (bytes): [0, 32768) partial absmax keys (uint32; one
+// reduction uses at most kMaxPartials of them, a pack set up to kWsPartials
+// in total), [32768, 33024) the weight path's {a, q, dq, 0}, one record per
 // weight of a pack set (room for 16).
 constexpr int kMaxPartials = 2048;
-constexpr size_t kWsScaleOffset = 8192;
-constexpr size_t kWsBytes = 8448;
+constexpr int kWsPartials = 8192;
+constexpr size_t kWsScaleOffset = 4 * (size_t)kWsPartials;
+constexpr size_t kWsBytes = kWsScaleOffset + 256;
 
 // A set of weights packed by one pass-1 and one pass-2 launch (kquant.hip):
-// weight i owns pass-1 workgroups [g1[i], g1[i+1]) (and their partial keys)
-// and pass-2 workgroups [g2[i], g2[i+1]); g1[count] <= kMaxPartials.
+// weight i owns pass-1 workgroups [g1[i], g1[i+1]) (and their partial keys,
+// at most kMaxPartials) and pass-2 workgroups [g2[i], g2[i+1]);
+// g1[count] <= kWsPartials.
 constexpr int kMaxPackSet = 8;
 struct PackSet {
     int count;
@@ -45,7 +48,7 @@ hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nblocks, uint8
 // Pass-1 workgroups (= partial keys) of one weight.
 int pack_absmax_groups(int qtype, uint64_t nb);
 // The two passes for `count` (<= kMaxPackSet) weights whose pass-1 groups
-// add up to at most kMaxPartials; weight i's scales go to ws +
+// add up to at most kWsPartials; weight i's scales go to ws +
 // kWsScaleOffset + 16 i and, when host_scale[i] is not null, to that host
 // memory followed by ticket[i].
 hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* blocks, const uint64_t* nb,

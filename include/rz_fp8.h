@@ -73,7 +73,7 @@ size_t rz_weight_bytes(int qtype, uint32_t n, uint32_t k);
  * buffer (gemm.rs page, cublas_prefill_fp8_gemm: M is padded to 16). */
 uint32_t rz_pad_m(uint32_t m);
 
-/* Size in bytes of the device workspace `ws` (a constant, a few KB). */
+/* Size in bytes of the device workspace `ws` (a constant, about 32 KB). */
 size_t rz_workspace_bytes(void);
 
 /*

@@ -164,12 +164,13 @@ def test_pack_weights_batch(rz):
 
 
 def test_pack_weights_sets_split_by_partial_keys(rz):
-    # 10752x3584 Q4_K weights take 1176 pass-1 workgroups each and the Q6_K one
-    # 588: the first two share a launch, the third needs its own (the partial
-    # keys of one launch are capped at 2048)
-    specs = [(W.Q4_K, 10752, 3584), (W.Q6_K, 5376, 3584), (W.Q4_K, 10752, 3584)]
+    # a 15360x3584 Q4_K weight takes 1680 pass-1 workgroups and a 7680x3584
+    # Q6_K one 840: the first five weights (7560 partial keys, mixed types)
+    # share one launch per pass, the sixth needs its own (a launch's partial
+    # keys are capped at 8192)
+    specs = [(W.Q4_K, 15360, 3584), (W.Q6_K, 7680, 3584)] + [(W.Q4_K, 15360, 3584)] * 4
     blocks = [W.weight_blocks(q, 1500 + i, n, k) for i, (q, n, k) in enumerate(specs)]
-    print("pack_weights: three large weights in two launch sets", flush=True)
+    print("pack_weights: six large weights in two launch sets", flush=True)
     outs = rz.rz_fp8_pack_weights([(q, dev(b), n, k, None) for (q, n, k), b in zip(specs, blocks)])
     for (q, n, k), b, (w8, scale, amax) in zip(specs, blocks, outs):
         r8, rdq, ra = fp8_path.pack_weight(q, b, n, k)
