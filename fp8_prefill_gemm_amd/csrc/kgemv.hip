@@ -27,6 +27,8 @@
 //      fp32 sums with fused multiply-adds, in K order; each activation value
 //      read from LDS serves RW rows.
 // A butterfly over the wave adds the 64 lane sums.  No workspace, no atomics.
+// For a single batch row (and Q6_K at two) a barrier-free variant reads the
+// activation straight into registers instead (kgemv_reg_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,6 +66,7 @@ constexpr int kLanesPerBlock = 8;                          // 32 weights per lan
 constexpr int kBlocksPerStep = kWave / kLanesPerBlock;     // blocks a wave covers per step
 constexpr int kSlotFloats = 36;                            // 32 values + 4 pad: slots 144 B apart
 constexpr int kBlockFloats = kLanesPerBlock * kSlotFloats; // LDS floats per block and batch row
+constexpr int kRegThreads = 256;                           // kgemv_reg_kernel group size
 
 // Where element e (0..255) of a super-block lives in the LDS slots: lane
 // (slot) u of the block and position in the slot.  Four consecutive elements
@@ -258,6 +261,74 @@ __global__ __launch_bounds__(WAVES* kWave) void kgemv_kernel(const uint8_t* __re
     if (active) store_sums<RW, MR>(acc, r0, n, y);
 }
 
+// The same product for the smallest batches without LDS or barriers: each
+// lane loads its two runs of 16 activation values per block straight from
+// global memory (they stay in L2) and uses them for the wave's RW rows; the
+// waves of a group are independent.  Lane u of a block covers the same
+// weights, in the same order, as in kgemv_kernel, so both give the same sums.
+template <int Q>
+__device__ __forceinline__ int run_a(int u) {  // first element of the lane's first run
+    if constexpr (Q == 12)
+        return 64 * (u >> 1) + 16 * (u & 1);
+    else
+        return 128 * (u >> 2) + 16 * ((u >> 1) & 1) + 32 * (u & 1);
+}
+template <int Q>
+constexpr int run_gap() {  // second run = first + gap
+    return Q == 12 ? 32 : 64;
+}
+
+template <int Q, int MR, int RW>
+__global__ __launch_bounds__(kRegThreads) void kgemv_reg_kernel(const uint8_t* __restrict__ blocks, uint32_t n,
+                                                                uint32_t nb, const float* __restrict__ x,
+                                                                uint32_t k, float* __restrict__ y) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t r0 = (blockIdx.x * (kRegThreads / kWave) + threadIdx.x / kWave) * RW;
+    if (r0 >= n) return;  // whole waves leave; no barriers
+    const int u = lane & (kLanesPerBlock - 1);
+    const int bl = lane / kLanesPerBlock;
+    const int xa = run_a<Q>(u);
+    const uint8_t* rowp[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        const uint32_t r = (r0 + i < n) ? r0 + i : n - 1;  // rows past n re-read the last row, not stored
+        rowp[i] = blocks + (size_t)r * nb * block_bytes<Q>();
+    }
+    float acc[RW][MR];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi) acc[i][mi] = 0.0f;
+    for (uint32_t b = bl; b < nb; b += kBlocksPerStep) {
+        Raw<Q> raw[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) load_raw(rowp[i] + (size_t)b * block_bytes<Q>(), u, raw[i]);
+        f32x4 xv[MR][8];
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi) {
+            const float* xb = x + (size_t)mi * k + (size_t)b * kQK + xa;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                xv[mi][c] = *reinterpret_cast<const f32x4*>(xb + 4 * c);
+                xv[mi][4 + c] = *reinterpret_cast<const f32x4*>(xb + run_gap<Q>() + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            float w[32];
+            decode_raw(raw[i], u, w);
+#pragma unroll
+            for (int mi = 0; mi < MR; ++mi) {
+                float a = acc[i][mi];
+#pragma unroll
+                for (int t = 0; t < 32; ++t) a = __builtin_fmaf(w[t], xv[mi][t >> 2][t & 3], a);
+                acc[i][mi] = a;
+            }
+        }
+    }
+    store_sums<RW, MR>(acc, r0, n, y);
+}
+
 // Launch shape (measured at N=4608, K=3584 Q4_K and N=3584, K=18944 Q6_K,
 // m = 1 and 4): chunks of 8 blocks (LDS = MR * 9216 B); 4 waves per group,
 // 8 for Q6_K at m >= 3; one row per wave except Q4_K at m >= 3 with
@@ -280,9 +351,32 @@ hipError_t launch_q(const uint8_t* blocks, uint32_t n, uint32_t nb, const float*
     return hipGetLastError();
 }
 
+template <int Q, int MR, int RW>
+hipError_t launch_reg(const uint8_t* blocks, uint32_t n, uint32_t nb, const float* x, uint32_t k, float* y,
+                      hipStream_t st) {
+    constexpr uint32_t kWavesPer = kRegThreads / kWave;
+    const uint32_t waves = (n + RW - 1) / RW;
+    kgemv_reg_kernel<Q, MR, RW><<<(waves + kWavesPer - 1) / kWavesPer, kRegThreads, 0, st>>>(blocks, n, nb, x, k, y);
+    return hipGetLastError();
+}
+
+// m = 1 (and Q6_K at m = 2) take the register kernel: measured 5.97 against
+// 6.52 us (Q4_K, N=4608, K=3584), 17.0 against 22.4 us (Q6_K, N=3584,
+// K=18944), 3.7 against 6.4 us (N=512); above that the LDS kernel's shared
+// activation reads win.
 template <int MR>
 hipError_t launch_mr(int qtype, const uint8_t* blocks, uint32_t n, uint32_t nb, const float* x, uint32_t k,
                      float* y, hipStream_t st) {
+    if constexpr (MR == 1) {
+        if (n < 2048u)  // few rows: one per wave keeps more waves in flight
+            return qtype == 12 ? launch_reg<12, 1, 1>(blocks, n, nb, x, k, y, st)
+                               : launch_reg<14, 1, 1>(blocks, n, nb, x, k, y, st);
+        return qtype == 12 ? launch_reg<12, 1, 2>(blocks, n, nb, x, k, y, st)
+                           : launch_reg<14, 1, 2>(blocks, n, nb, x, k, y, st);
+    }
+    if constexpr (MR == 2) {
+        if (qtype == 14) return launch_reg<14, 2, 2>(blocks, n, nb, x, k, y, st);
+    }
     if (qtype == 14) return launch_q<14, MR, 1, MR <= 2 ? 4 : 8>(blocks, n, nb, x, k, y, st);
     if (MR >= 3 && n >= 4096u) return launch_q<12, MR, 2, 4>(blocks, n, nb, x, k, y, st);
     return launch_q<12, MR, 1, 4>(blocks, n, nb, x, k, y, st);
