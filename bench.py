@@ -28,6 +28,9 @@ blocks -> 6.53 GB of E4M3 codes) after a 1 GiB write that evicts the caches:
 all 196 weights in one rz_fp8_pack_weights call, and, for comparison, 196
 rz_fp8_pack_weight calls back to back; it prints that measurement's own line.
 
+--gemm-shapes instead times the FP8 GEMM alone at every configuration's
+shapes (warm, random E4M3 codes) and the 28-layer M=4096 sweep from them.
+
 --small-m instead times the small-batch routes (GEMV straight from K-quant
 blocks, FP8 GEMM, activation quantisation + FP8 GEMM) at N=4608, K=3584.
 """
@@ -253,6 +256,65 @@ def small_m(args, dev) -> int:
     return 0
 
 
+def gemm_shapes(args, dev) -> int:
+    """Warm FP8 GEMM time per shape of the five configurations (one line):
+    random E4M3 codes (no NaN codes), scales 1, the library's default
+    workspace, HIP events around 20 launches after 5 warm-up launches.  Also
+    the 28-layer sweep at M=4096 (7 GEMMs per layer, 53.46 TFLOP) from the
+    per-shape times."""
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+
+    H, KV, F = 3584, 512, 18944
+    shapes = [("cfg1", 16, 256, 512), ("cfg2 q", 512, H, H), ("cfg2 k/v", 512, KV, H),
+              ("cfg3 gate/up", 2048, F, H), ("cfg3 down", 2048, H, F),
+              ("cfg4 q/o", 4096, H, H), ("cfg4 k/v", 4096, KV, H), ("cfg4 gate/up", 4096, F, H),
+              ("cfg4 down", 4096, H, F), ("cfg5 m=1", 1, 4608, H), ("cfg5 m=4", 4, 4608, H),
+              ("cfg5 m=37", 37, 4608, H), ("cfg5 m=1000", 1000, 4608, H)]
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def codes(rows, cols):
+        c = torch.randint(0, 256, (rows, cols), dtype=torch.int32, device=dev, generator=g)
+        c = torch.where((c & 0x7F) == 0x7F, c - 1, c)  # 0x7F / 0xFF are E4M3FN NaN codes
+        return c.to(torch.uint8)
+
+    sc = torch.ones(2, dtype=torch.float32, device=dev)
+    rows = {}
+    for name, m, n, k in shapes:
+        a = codes(rz.rz_pad_m(m), k)
+        w = codes(n, k)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            rz.rz_fp8_gemm(a, w, m, sc, 1.0, y, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            rz.rz_fp8_gemm(a, w, m, sc, 1.0, y, stream)
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 20
+        plan = rz.rz_fp8_gemm_plan(m, n, k)
+        byts = n * k + rz.rz_pad_m(m) * k + 4 * m * n
+        rows[name] = {"m": m, "n": n, "k": k, "us": round(t * 1e6, 2),
+                      "tflops": round(2.0 * m * n * k / t / 1e12, 1), "gb_s": round(byts / t / 1e9, 1),
+                      "plan": {"bn": plan[0], "bm": plan[1], "threads": plan[2], "workgroups": plan[3]}}
+        log(f"{name}: {rows[name]}")
+        del a, w, y
+    per_layer = sum(rows[nm]["us"] * c for nm, c in (("cfg4 q/o", 2), ("cfg4 k/v", 2), ("cfg4 gate/up", 2),
+                                                       ("cfg4 down", 1))) * 1e-6
+    sweep_flop = 28 * 2.0 * 4096 * (2 * H * H + 2 * KV * H + 2 * F * H + H * F)
+    out = {"metric": "FP8 GEMM per shape (warm, random E4M3 codes)", "unit": "us", "higher_is_better": False,
+           "rows": rows, "sweep_28_layers_m4096": {"ms": round(28 * per_layer * 1e3, 3),
+                                                   "tflop": round(sweep_flop / 1e12, 2),
+                                                   "tflops": round(sweep_flop / (28 * per_layer) / 1e12, 1)},
+           "data": "synthetic", "config": {"workload": "GEMM shapes of the five configurations"}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +327,8 @@ def main() -> int:
     ap.add_argument("--pack-model", action="store_true",
                     help="time the cold-cache packing of all 196 weights of the 28-layer sweep instead")
     ap.add_argument("--pack-repeats", type=int, default=3, help="cold passes of --pack-model")
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="instead time the FP8 GEMM alone at every configuration's shapes (warm)")
     ap.add_argument("--small-m", type=int, nargs="*", default=None,
                     help="instead time the small-batch paths at N=4608, K=3584 (Q4_K) for these m")
     args = ap.parse_args()
@@ -290,6 +354,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.pack_model:
         return pack_model(args, dev)
+    if args.gemm_shapes:
+        return gemm_shapes(args, dev)
     if args.small_m is not None:
         if not args.small_m:
             args.small_m = [1, 2, 3, 4, 8, 37]
