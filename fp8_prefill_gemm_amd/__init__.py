@@ -44,6 +44,7 @@ _SIGS = {
     "rz_fp8_quant_act": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp, _vp]),
     "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
+    "rz_fp8_gemm_group": (_i32, [_vp, _u32, _u32, _vp, _u32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_dequant_f32": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
     "rz_absmax_f32": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_e4m3_encode": (_i32, [_vp, _u64, _f32, _vp, _vp]),
@@ -251,6 +252,33 @@ def rz_kquant_gemv(qtype: int, blocks, n: int, k: int, x, y=None, stream=None):
         y = torch.empty((m, n), dtype=torch.float32, device=blocks.device)
     _check(lib().rz_kquant_gemv(qtype, _ptr(blocks), n, k, _ptr(x), m, _ptr(y), _stream(stream, blocks.device)))
     return y
+
+
+def rz_fp8_gemm_group(a_fp8, m: int, act_scale, weights, ys=None, stream=None, ws="auto"):
+    """weights: sequence of (w_fp8 uint8 [n][k], w_scale) sharing the FP8
+    activation a_fp8 -> list of y fp32 [m][n], in one launch when the shapes
+    allow it (see include/rz_fp8.h)."""
+    torch = _torch()
+    weights = list(weights)
+    cnt = len(weights)
+    _require_cuda(a_fp8, act_scale, *[w for w, _ in weights])
+    k = a_fp8.shape[1]
+    dev = a_fp8.device
+    if ys is None:
+        ys = [torch.empty((m, w.shape[0]), dtype=torch.float32, device=dev) for w, _ in weights]
+    _require_cuda(*ys)
+    if isinstance(ws, str):
+        need = max([rz_fp8_gemm_workspace_bytes(m, w.shape[0], k) for w, _ in weights] + [0])
+        ws = gemm_workspace(dev, need) if need else None
+    _require_cuda(ws)
+    wp = (ctypes.c_void_p * max(cnt, 1))(*[_ptr(w) for w, _ in weights])
+    nn = (ctypes.c_uint32 * max(cnt, 1))(*[w.shape[0] for w, _ in weights])
+    sc = (ctypes.c_float * max(cnt, 1))(*[float(s) for _, s in weights])
+    yp = (ctypes.c_void_p * max(cnt, 1))(*[_ptr(y) for y in ys])
+    _check(lib().rz_fp8_gemm_group(_ptr(a_fp8), m, k, _ptr(act_scale), cnt, ctypes.addressof(wp),
+                                   ctypes.addressof(nn), ctypes.addressof(sc), ctypes.addressof(yp), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream, dev)))
+    return ys
 
 
 def rz_dequant_f32(qtype: int, blocks, n: int, k: int, out=None, stream=None):

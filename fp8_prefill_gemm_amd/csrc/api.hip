@@ -345,6 +345,64 @@ int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
+int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float* act_scale_dev, uint32_t count,
+                      const uint8_t* const* w_fp8, const uint32_t* n, const float* w_scale, float* const* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rz_fp8_gemm_group";
+    if (int r = check_k(fn, k)) return r;
+    if (k > RZ_MAX_GEMM_K) return fail(RZ_ERR_SHAPE, "%s: k=%u exceeds %u", fn, k, (unsigned)RZ_MAX_GEMM_K);
+    if (count > RZ_GEMM_GROUP_MAX) return fail(RZ_ERR_SHAPE, "%s: count=%u exceeds %u", fn, count, (unsigned)RZ_GEMM_GROUP_MAX);
+    if (count == 0 || m == 0) return RZ_OK;  // nothing to read or write
+    if (!w_fp8 || !n || !w_scale || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (!a_fp8 || !act_scale_dev) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || m > 0x7FFFFFF0u) return fail(RZ_ERR_SHAPE, "%s: operand too large", fn);
+    if (!aligned16(a_fp8) || ((uintptr_t)act_scale_dev & 3u) || (ws && !aligned16(ws)))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    uint64_t ntot = 0;
+    bool whole = true;  // every width a multiple of 256: the GEMMs can share one launch
+    for (uint32_t i = 0; i < count; ++i) {
+        if (n[i] == 0) continue;
+        if (!w_fp8[i] || !y[i]) return fail(RZ_ERR_NULL, "%s: gemm %u: null pointer", fn, i);
+        if ((uint64_t)n[i] * k > RZ_MAX_ELEMS || (uint64_t)m * n[i] > RZ_MAX_ELEMS || n[i] > 0x7FFFFFF0u)
+            return fail(RZ_ERR_SHAPE, "%s: gemm %u: operand too large", fn, i);
+        if (!aligned16(w_fp8[i]) || !aligned16(y[i]))
+            return fail(RZ_ERR_ALIGN, "%s: gemm %u: device pointers must be 16-byte aligned", fn, i);
+        if (w_scale[i] != w_scale[i] || w_scale[i] - w_scale[i] != 0.0f)
+            return fail(RZ_ERR_VALUE, "%s: gemm %u: w_scale must be finite", fn, i);
+        whole = whole && n[i] % 256u == 0;
+        ntot += n[i];
+    }
+    if (ntot == 0) return RZ_OK;
+    if (int r = check_device(fn)) return r;
+    hipStream_t st = as_stream(stream);
+    const int cus = device_cus();
+    if (whole && ntot < (1u << 21)) {
+        const rz::GemmPlan p = rz::plan_gemm(m, (uint32_t)ntot, k, cus, true);
+        if (p.kind == rz::kGemmTiles) {  // one launch over the concatenated widths
+            rz::GemmGroups G = {};
+            int end = 0;
+            for (uint32_t i = 0; i < count; ++i) {
+                if (n[i] == 0) continue;
+                end += (int)n[i];
+                G.n_end[G.count] = end;
+                G.w[G.count] = w_fp8[i];
+                G.y[G.count] = y[i];
+                G.w_scale[G.count] = w_scale[i];
+                ++G.count;
+            }
+            const hipError_t e = rz::launch_interior(p, a_fp8, G, m, (uint32_t)ntot, k, act_scale_dev, st);
+            return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+        }
+    }
+    for (uint32_t i = 0; i < count; ++i) {  // one launch per GEMM, in order on the stream
+        if (n[i] == 0) continue;
+        const hipError_t e = rz::launch_gemm(a_fp8, w_fp8[i], m, n[i], k, act_scale_dev, w_scale[i], y[i], ws,
+                                             ws ? ws_bytes : 0, cus, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return RZ_OK;
+}
+
 size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k) {
     if (k == 0 || k % 256u != 0 || m == 0 || n == 0) return 0;
     return rz::plan_gemm(m, n, k, device_cus(), true).ws_bytes;

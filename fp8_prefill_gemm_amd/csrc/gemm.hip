@@ -299,10 +299,22 @@ __device__ __forceinline__ bool xcd_item(int w, int T, int& t) {
     return true;
 }
 
-__global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* __restrict__ A,
-                                                                const uint8_t* __restrict__ Wt, float* __restrict__ Y,
+// The weight and output of the n-tile starting at column n0 of the launch:
+// the launch's N columns are the groups' columns one after the other (every
+// group boundary a multiple of 256 when there are several groups, so a tile
+// never straddles two).  n0 becomes the column inside the group, N its width.
+__device__ __forceinline__ int group_of(const GemmGroups& G, int& n0, int& N) {
+    int g = 0;
+    while (g + 1 < G.count && n0 >= G.n_end[g]) ++g;
+    const int begin = g ? G.n_end[g - 1] : 0;
+    n0 -= begin;
+    N = G.n_end[g] - begin;
+    return g;
+}
+
+__global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* __restrict__ A, GemmGroups G,
                                                                 int M, int N, int K,
-                                                                const float* __restrict__ act_scale, float w_scale,
+                                                                const float* __restrict__ act_scale,
                                                                 InteriorPlan P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
 
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     const int wn = wid & 1, wm = wid >> 1;
     const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
     const uint32_t step = 32u * (uint32_t)K;
-    const float scale = act_scale[1] * w_scale;
+    const float act_dq = act_scale[1];
     const int mp = (M + 15) & ~15;  // >= 256 here
     int t, n0, m0;
     if (bid < P.nwhole) {
@@ -321,11 +333,14 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
         grouped_origin_bb<256, 256>(t, P.tiles_m, P.nd, P.group_m, n0, m0);
         m0 = m0 < mp - 256 ? m0 : mp - 256;
         n0 = n0 < N - 256 ? n0 : N - 256;
+        int Ng;
+        const int g = group_of(G, n0, Ng);
         const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
         v16f acc[4][4];
-        tile_mainloop<4>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+        tile_mainloop<4>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
                          tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
-        store_acc<4>(acc, tile_out_rsrc(Y, M, N, m0), (uint32_t)N, (uint32_t)n0, wn, wm, lane, scale);
+        store_acc<4>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
+                     act_dq * G.w_scale[g]);
         return;
     }
     // nwhole is a multiple of 8: the half tiles' workgroups keep w % 8
@@ -334,11 +349,14 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     m0 = m0 < mp - 128 ? m0 : mp - 128;
     n0 += P.nd * 256;
     n0 = n0 < N - 256 ? n0 : N - 256;
+    int Ng;
+    const int g = group_of(G, n0, Ng);
     const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
     v16f acc[4][2];
-    tile_mainloop<2>(acc, smem, tile_rsrc(Wt + (size_t)n0 * K, 256u * (uint32_t)K),
+    tile_mainloop<2>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
                      tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
-    store_acc<2>(acc, tile_out_rsrc(Y, M, N, m0), (uint32_t)N, (uint32_t)n0, wn, wm, lane, scale);
+    store_acc<2>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
+                 act_dq * G.w_scale[g]);
 }
 
 struct KindInfo {
@@ -445,6 +463,17 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
         p = plan_gemm(m, n, k, cus, false);  // no room for partial sums: whole tiles only
     if (p.kind != kGemmTiles) return launch_gemm_edge(p, a_fp8, w_fp8, m, n, k, act_scale, w_scale, y, ws, st);
+    GemmGroups G = {};
+    G.count = 1;
+    G.n_end[0] = (int)n;
+    G.w[0] = w_fp8;
+    G.y[0] = y;
+    G.w_scale[0] = w_scale;
+    return launch_interior(p, a_fp8, G, m, n, k, act_scale, st);
+}
+
+hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGroups& G, uint32_t m, uint32_t n,
+                           uint32_t k, const float* act_scale, hipStream_t st) {
     const int mp = (int)((m + 15u) & ~15u);
     const int tiles_m = ceil_div(mp, 256);
     InteriorPlan ip;
@@ -461,8 +490,8 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     int hgm = 1;
     while (hgm * 2 <= ip.halves_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
     ip.half_gm = hgm;
-    fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, w_fp8, y, (int)m, (int)n,
-                                                                             (int)k, act_scale, w_scale, ip);
+    fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n, (int)k,
+                                                                             act_scale, ip);
     return hipGetLastError();
 }
 

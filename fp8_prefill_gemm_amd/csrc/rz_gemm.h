@@ -20,6 +20,22 @@ struct GemmPlan {
     size_t ws_bytes;  // workspace the plan needs (0: none)
 };
 GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed);
+// Weights and outputs of the GEMMs one interior launch computes on a shared
+// activation: group g owns columns [n_end[g-1], n_end[g]) of the launch
+// (n_end[-1] = 0), with its own weight rows, fp32 output [M][width] and
+// weight scale.  With several groups every n_end is a multiple of 256.
+constexpr int kMaxGemmGroups = 4;
+struct GemmGroups {
+    int count;
+    int n_end[kMaxGemmGroups];
+    const uint8_t* w[kMaxGemmGroups];
+    float* y[kMaxGemmGroups];
+    float w_scale[kMaxGemmGroups];
+};
+// The interior-tile kernel (p.kind == kGemmTiles, p planned for the total
+// width n = G.n_end[G.count - 1]).
+hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGroups& G, uint32_t m, uint32_t n,
+                           uint32_t k, const float* act_scale, hipStream_t st);
 hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                        uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
                        size_t ws_bytes, int cus, hipStream_t st);

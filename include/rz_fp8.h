@@ -170,6 +170,36 @@ int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t
                 uint32_t k, const float* act_scale_dev, float w_scale, float* y,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Largest number of GEMMs one rz_fp8_gemm_group call takes. */
+#define RZ_GEMM_GROUP_MAX 4u
+
+/*
+ * Several FP8 GEMMs on one quantised activation (gemm.rs page,
+ * cublas_prefill_fp8_gemm: the Q/K/V projections, and the FFN gate and up
+ * projections, share one activation conversion), as `count` rz_fp8_gemm
+ * calls would compute them:
+ *
+ *   y[g][i][j] = (sum_k dec(a_fp8[i][kk]) * dec(w_fp8[g][j][kk]))
+ *                * act_scale_dev[1] * w_scale[g]      for i < m, j < n[g]
+ *
+ *   a_fp8, m, k, act_scale_dev   the shared activation, as for rz_fp8_gemm
+ *   w_fp8, n, w_scale, y         host arrays of `count` (<= RZ_GEMM_GROUP_MAX)
+ *                 entries: weight g (device, uint8 [n[g]][k]), its host
+ *                 scale, and its output (device, fp32 [m][n[g]]); n[g] == 0
+ *                 skips that GEMM (its pointers may then be NULL)
+ *   ws, ws_bytes  as for rz_fp8_gemm (used only when the GEMMs run one by one)
+ * When every n[g] is a multiple of 256 and the combined width takes the
+ * 256x256 interior-tile kernel, all the GEMMs run as one launch (their
+ * tiles share the rounds of the compute units, so the partial last round is
+ * paid once); each output element is then computed exactly as rz_fp8_gemm's
+ * interior kernel computes it.  Otherwise the GEMMs run one after another
+ * as rz_fp8_gemm would run them.  m == 0 or count == 0 is a no-op.
+ */
+int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float* act_scale_dev,
+                      uint32_t count, const uint8_t* const* w_fp8, const uint32_t* n,
+                      const float* w_scale, float* const* y, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Workspace rz_fp8_gemm can use for this shape on the current device
  * (0 when it would not split). */
 size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k);

@@ -161,6 +161,33 @@ def test_kquant_gemv_validation(L):
     assert f(12, None, 0, 255, None, 4, None) == RZ_ERR_SHAPE
 
 
+def test_gemm_group_validation(L):
+    V = ctypes.c_void_p
+    arr = lambda ct, vals: (ct * len(vals))(*vals)
+
+    def f(a, m, k, sc, cnt, w, n, s, y):
+        return L.rz_fp8_gemm_group(a, m, k, sc, cnt, w, n, s, y, None, 0, None)
+    w = arr(V, [P, P2])
+    n = arr(ctypes.c_uint32, [256, 512])
+    s = arr(ctypes.c_float, [1.0, 2.0])
+    y = arr(V, [P3, P])
+    assert f(P, 4, 256, P3, 0, None, None, None, None) == RZ_OK
+    assert f(P, 0, 256, P3, 2, w, n, s, y) == RZ_OK
+    assert f(P, 4, 256, P3, 5, w, n, s, y) == RZ_ERR_SHAPE
+    assert f(P, 4, 300, P3, 2, w, n, s, y) == RZ_ERR_SHAPE
+    assert f(None, 4, 256, P3, 2, w, n, s, y) == RZ_ERR_NULL
+    assert f(P, 4, 256, None, 2, w, n, s, y) == RZ_ERR_NULL
+    assert f(P, 4, 256, P3, 2, None, n, s, y) == RZ_ERR_NULL
+    assert f(P, 4, 256, P3, 2, arr(V, [P, None]), n, s, y) == RZ_ERR_NULL
+    assert "gemm 1" in _err(L)
+    assert f(BAD, 4, 256, P3, 2, w, n, s, y) == RZ_ERR_ALIGN
+    assert f(P, 4, 256, P3, 2, w, n, s, arr(V, [P3, BAD])) == RZ_ERR_ALIGN
+    assert f(P, 4, 256, P3, 2, w, n, arr(ctypes.c_float, [1.0, float("nan")]), y) == RZ_ERR_VALUE
+    # zero-width GEMMs are skipped: nothing to launch, no device needed
+    assert f(P, 4, 256, P3, 2, arr(V, [None, None]), arr(ctypes.c_uint32, [0, 0]), s,
+             arr(V, [None, None])) == RZ_OK
+
+
 def test_gemm_workspace_sizes(L):
     # the GEMV and skinny kernels (padded M <= 64) need none; split-K with 64x32 tiles:
     # 256 bytes of arrival counters + 12 tiles x 2 chunks of 64x32 fp32

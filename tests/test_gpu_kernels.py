@@ -460,6 +460,55 @@ def test_gemm_edge_split_plans(rz, m, n, k, full):
     assert (host(ws[:4 * tiles]) == 0).all()  # arrival counters left at zero for the next call
 
 
+@pytest.mark.parametrize("m,k,ns", [
+    (2048, 1024, (18944, 18944)),    # gate/up widths: one launch of 1184 tiles (all whole)
+    (4096, 512, (3584, 512, 512)),   # q/k/v widths at M=4096: 288 tiles, one round + half tiles
+    (2000, 512, (2560, 1024, 256)),  # ragged M, groups of 10, 4 and 1 n-tiles
+    (4096, 512, (1024, 0, 512, 2048)),  # a skipped (zero-width) GEMM
+])
+def test_gemm_group_one_launch(rz, m, k, ns):
+    # the grouped launch computes every element exactly as a single call's
+    # interior kernel does; the widths here take the interior plan on their own
+    # too, except where noted, and some rows are checked against the oracle
+    g = np.random.Generator(np.random.PCG64(m + k + len(ns)))
+    mp = fp8_path.pad_m(m)
+    a8 = _codes(g, (mp, k))
+    a8[m:] = 0
+    ws_ = [_codes(g, (n, k)) for n in ns]
+    scales = [0.25 + 0.125 * i for i in range(len(ns))]
+    sc = np.array([1.0, 0.5, 0, 0], np.float32)
+    A, S = dev(a8), dev(sc)
+    print(f"gemm_group m={m} k={k} ns={ns}", flush=True)
+    ys = rz.rz_fp8_gemm_group(A, m, S, [(dev(w), s) for w, s in zip(ws_, scales)])
+    rows = np.unique(np.concatenate([[0, 1, m - 2, m - 1], g.integers(0, m, 12)]))
+    for w, s, y in zip(ws_, scales, ys):
+        n = w.shape[0]
+        assert tuple(y.shape) == (m, n)
+        if n == 0:
+            continue
+        got = host(y)
+        single = host(rz.rz_fp8_gemm(A, dev(w), m, S, s))
+        if rz.rz_fp8_gemm_plan(m, n, k)[:2] == (256, 256):
+            np.testing.assert_array_equal(got, single)
+        check_gemm(got[rows], a8[rows], w, len(rows), sc[1], np.float32(s))
+
+
+def test_gemm_group_falls_back_to_single_calls(rz):
+    # widths that are not multiples of 256, and a small M: one call per GEMM,
+    # the same results as those calls
+    for m, k, ns in ((2048, 512, (2500, 512)), (64, 512, (1024, 768)), (512, 3584, (3584, 512, 512))):
+        g = np.random.Generator(np.random.PCG64(m * 3 + k))
+        a8 = _codes(g, (fp8_path.pad_m(m), k))
+        a8[m:] = 0
+        ws_ = [_codes(g, (n, k)) for n in ns]
+        sc = np.array([1.0, 0.75, 0, 0], np.float32)
+        A, S = dev(a8), dev(sc)
+        print(f"gemm_group fallback m={m} k={k} ns={ns}", flush=True)
+        ys = rz.rz_fp8_gemm_group(A, m, S, [(dev(w), 0.5) for w in ws_])
+        for w, y in zip(ws_, ys):
+            np.testing.assert_array_equal(host(y), host(rz.rz_fp8_gemm(A, dev(w), m, S, 0.5)))
+
+
 def test_gemm_identity_weight(rz):
     k, n, m = 512, 64, 37
     w8 = np.zeros((n, k), np.uint8)
