@@ -7,14 +7,14 @@ weights, K=3584):
   down     : K=18944, N=3584,  Q6_K, input SiLU(g)*u
 One step is one pass of the whole path over that batch: pack the three
 weights (dequantise, absmax, E4M3 encode) in one call with one host wait for
-their scales, quantise the FFN input once for gate and up, run gate and up,
-quantise the down input, run down.  Inputs are synthetic (seeded), resident in
+their scales, quantise the FFN input once for gate and up, run gate and up
+(one grouped launch), quantise the down input, run down.  Inputs are synthetic (seeded), resident in
 HBM before timing.
 
 value = GEMM FLOPs of the step (3 x 2*M*N*K) / measured step time, TFLOP/s.
-roofline = the gate/up GEMM kernel (2*M*N*K per launch) timed with HIP
-events on its own stream during the timed steps (the only markers in the
-timed loop), against the 5.0 PFLOP/s dense FP8 peak.  phases_us comes from a
+roofline = the gate+up GEMM launch (one rz_fp8_gemm_group call, 2 x 2*M*N*K
+per launch) timed with HIP events on its stream during the timed steps (the
+only markers in the timed loop), against the 5.0 PFLOP/s dense FP8 peak.  phases_us comes from a
 second, untimed pass of the same steps with markers between all phases.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload (see
 --help).
@@ -303,13 +303,40 @@ def gemm_shapes(args, dev) -> int:
                       "plan": {"bn": plan[0], "bm": plan[1], "threads": plan[2], "workgroups": plan[3]}}
         log(f"{name}: {rows[name]}")
         del a, w, y
+    # GEMMs that share an activation, in one rz_fp8_gemm_group launch
+    groups = [("cfg3 gate+up grouped", 2048, (F, F), H), ("cfg4 q+k+v grouped", 4096, (H, KV, KV), H),
+              ("cfg4 gate+up grouped", 4096, (F, F), H)]
+    for name, m, ns, k in groups:
+        a = codes(rz.rz_pad_m(m), k)
+        ws_ = [(codes(n, k), 1.0) for n in ns]
+        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for n in ns]
+        for _ in range(5):
+            rz.rz_fp8_gemm_group(a, m, sc, ws_, ys, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            rz.rz_fp8_gemm_group(a, m, sc, ws_, ys, stream)
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 20
+        plan = rz.rz_fp8_gemm_plan(m, sum(ns), k)
+        rows[name] = {"m": m, "n": list(ns), "k": k, "us": round(t * 1e6, 2),
+                      "tflops": round(2.0 * m * sum(ns) * k / t / 1e12, 1),
+                      "plan": {"bn": plan[0], "bm": plan[1], "threads": plan[2], "workgroups": plan[3]}}
+        log(f"{name}: {rows[name]}")
+        del a, ws_, ys
     per_layer = sum(rows[nm]["us"] * c for nm, c in (("cfg4 q/o", 2), ("cfg4 k/v", 2), ("cfg4 gate/up", 2),
                                                        ("cfg4 down", 1))) * 1e-6
+    per_layer_grouped = sum(rows[nm]["us"] for nm in ("cfg4 q+k+v grouped", "cfg4 q/o", "cfg4 gate+up grouped",
+                                                       "cfg4 down")) * 1e-6
     sweep_flop = 28 * 2.0 * 4096 * (2 * H * H + 2 * KV * H + 2 * F * H + H * F)
     out = {"metric": "FP8 GEMM per shape (warm, random E4M3 codes)", "unit": "us", "higher_is_better": False,
            "rows": rows, "sweep_28_layers_m4096": {"ms": round(28 * per_layer * 1e3, 3),
                                                    "tflop": round(sweep_flop / 1e12, 2),
                                                    "tflops": round(sweep_flop / (28 * per_layer) / 1e12, 1)},
+           "sweep_28_layers_m4096_grouped": {"ms": round(28 * per_layer_grouped * 1e3, 3),
+                                             "tflops": round(sweep_flop / (28 * per_layer_grouped) / 1e12, 1),
+                                             "note": "q+k+v and gate+up as one launch each, o and down alone"},
            "data": "synthetic", "config": {"workload": "GEMM shapes of the five configurations"}}
     print(json.dumps(out), flush=True)
     return 0
@@ -396,13 +423,13 @@ def main() -> int:
         log("copy calibration: 1 GiB read + 1 GiB write done")
         del src, dst
 
-    phases = ["pack", "quant_ffn", "gemm_gate", "gemm_up", "quant_down", "gemm_down"]
+    phases = ["pack", "quant_ffn", "gemm_gate_up", "quant_down", "gemm_down"]
     packs = [(g.qtype, blk, g.n, g.k, w8[g.name]) for g, blk in ((gate, b_gate), (up, b_up), (dn, b_down))]
 
     def step(events=None, gemm_events=None):
-        """One pass of the path.  events: 7 markers between the phases
-        (diagnostic pass); gemm_events: 2 markers, before the gate GEMM and
-        after the up GEMM (timed pass, for the roofline)."""
+        """One pass of the path.  events: 6 markers between the phases
+        (diagnostic pass); gemm_events: 2 markers around the gate+up GEMM
+        launch (timed pass, for the roofline)."""
         def mark(i):
             if events is not None:
                 events[i].record(stream)
@@ -416,15 +443,15 @@ def main() -> int:
         rz.rz_fp8_quant_act(x_ffn, a8_ffn, sc_ffn, ws, stream)
         mark(2)
         gmark(0)
-        rz.rz_fp8_gemm(a8_ffn, w8["gate"], M, sc_ffn, s_gate, y["gate"], stream, gws)
+        # gate and up share the FP8 activation: one launch for both
+        rz.rz_fp8_gemm_group(a8_ffn, M, sc_ffn, [(w8["gate"], s_gate), (w8["up"], s_up)],
+                             [y["gate"], y["up"]], stream, gws)
         mark(3)
-        rz.rz_fp8_gemm(a8_ffn, w8["up"], M, sc_ffn, s_up, y["up"], stream, gws)
-        mark(4)
         gmark(1)
         rz.rz_fp8_quant_act(x_down, a8_down, sc_down, ws, stream)
-        mark(5)
+        mark(4)
         rz.rz_fp8_gemm(a8_down, w8["down"], M, sc_down, s_down, y["down"], stream, gws)
-        mark(6)
+        mark(5)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -440,10 +467,10 @@ def main() -> int:
         step(gemm_events=gev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gateup_events_us = float(np.mean([0.5 * e[0].elapsed_time(e[1]) for e in gev])) * 1e3
+    gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev])) * 1e3
 
     # diagnostic pass (not timed as a whole): markers between every phase
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(events=ev[i])
     torch.cuda.synchronize()
@@ -453,10 +480,11 @@ def main() -> int:
     flop = {g.name: 2.0 * M * g.n * g.k for g in (gate, up, dn)}
     step_flop = sum(flop.values())
     value = step_flop / (ms_per_step * 1e-3) / 1e12
-    gemm_tflops = {n: flop[n] / (ph["gemm_" + n] * 1e-6) / 1e12 for n in flop}
-    gateup_us = gateup_events_us
-    achieved = flop["gate"] / (gateup_us * 1e-6) / 1e12
-    plan = rz.rz_fp8_gemm_plan(M, gate.n, gate.k)
+    gemm_tflops = {"gate_up": (flop["gate"] + flop["up"]) / (ph["gemm_gate_up"] * 1e-6) / 1e12,
+                   "down": flop["down"] / (ph["gemm_down"] * 1e-6) / 1e12}
+    gateup_us = gateup_events_us  # the one launch of both GEMMs
+    achieved = (flop["gate"] + flop["up"]) / (gateup_us * 1e-6) / 1e12
+    plan = rz.rz_fp8_gemm_plan(M, gate.n + up.n, gate.k)
     # HBM-bound phases: algorithmic bytes (blocks read twice + 1 B per weight
     # written; activations read twice as fp32 + 1 B per element written)
     # against the 8 TB/s HBM peak
@@ -471,7 +499,7 @@ def main() -> int:
                "frac": round(b / (ph[k] * 1e-6) / 1e12 / HBM_PEAK_TBPS, 4)} for k, b in algo.items()}
     log("phases (us): " + " ".join(f"{k}={v:.1f}" for k, v in ph.items()))
     log("HBM-bound phases: " + " ".join(f"{k}={v['tb_per_s']:.2f}TB/s({v['frac']:.0%})" for k, v in hbm.items()))
-    log(f"gate/up GEMM {gateup_us:.1f} us = {achieved:.1f} TFLOP/s ({achieved / FP8_PEAK_TFLOPS:.1%} of peak), "
+    log(f"gate+up GEMM launch {gateup_us:.1f} us = {achieved:.1f} TFLOP/s ({achieved / FP8_PEAK_TFLOPS:.1%} of peak), "
         f"plan BNxBM={plan[0]}x{plan[1]} threads={plan[2]} wgs={plan[3]}")
 
     out = {
@@ -493,7 +521,8 @@ def main() -> int:
             "m": M, "gate_up": [gate.n, gate.k], "down": [dn.n, dn.k],
         },
         "roofline": {
-            "kernel": f"gate/up GEMM, {plan[0]}x{plan[1]} tiles (M=2048 N=18944 K=3584)",
+            "kernel": (f"gate+up GEMM in one launch, {plan[0]}x{plan[1]} tiles, {plan[3]} workgroups "
+                       f"(M=2048, N=2x18944, K=3584)"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP8_PEAK_TFLOPS,
