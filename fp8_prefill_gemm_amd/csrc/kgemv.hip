@@ -340,9 +340,12 @@ hipError_t launch_q(const uint8_t* blocks, uint32_t n, uint32_t nb, const float*
                     hipStream_t st) {
     constexpr size_t lds = (size_t)MR * kChunkBlocks * kBlockFloats * sizeof(float);
     auto kern = kgemv_kernel<Q, MR, RW, kChunkBlocks, WAVES>;
-    if constexpr (lds > 65536) {  // m = 8: 72 KB of the 160 KB per CU, opted in once per kernel
-        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if constexpr (lds > 65536) {
+        // m = 8: 72 KB of the 160 KB per CU.  The opt-in is set at every such
+        // launch (a host-side attribute, cheap), so it holds on whichever
+        // device is current.
+        const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (attr != hipSuccess) return attr;
     }
     const uint32_t waves = (n + RW - 1) / RW;
