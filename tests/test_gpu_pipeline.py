@@ -1,7 +1,10 @@
 """End-to-end parity of the path on the workload configurations (GPU).
 
 Each group quantises its activation once and reuses it for every GEMM that
-reads it (Q/K/V; gate/up), as the path prescribes.  Packed bytes, scales and
+reads it (Q/K/V; gate/up), as the path prescribes: either one GEMM call per
+weight, or (the way bench.py runs the FFN step) every weight of the step
+packed by one rz_fp8_pack_weights call and the GEMMs on one activation run
+by one rz_fp8_gemm_group call.  Packed bytes, scales and
 activation codes are compared bit for bit with the oracle; GEMM outputs are
 compared element by element on every row for the small configurations and
 on sampled rows (the oracle computes those rows exactly) at full size.
@@ -59,6 +62,43 @@ def run_group(rz, grp, rows=None, check_bytes=True):
         del w8, y
 
 
+def check_rows(name, y, r8, rw8, rdq, rwdq, sel):
+    y_s = y[torch.from_numpy(np.asarray(sel)).cuda()].cpu().numpy().astype(np.float64)
+    yr, tol = fp8_path.gemm_rows(r8, rw8, np.asarray(sel), rdq, rwdq)
+    err = np.abs(y_s - yr)
+    assert (err <= tol).all(), f"{name}: {(err > tol).sum()} out of bound"
+    assert np.isfinite(y_s).all()
+    print(f"    {name}: rows={len(sel)} max err/tol={np.max(err / np.where(tol > 0, tol, 1)):.3g}", flush=True)
+
+
+def run_step(rz, groups, rows=None):
+    """The groups' weights packed in one call; per group one activation
+    quantisation and one grouped GEMM call; every result against the oracle."""
+    ws = rz.workspace("cuda")
+    gemms = [gm for grp in groups for gm in grp.gemms]
+    print(f"\n  step: {[(gm.name, gm.n, gm.k) for gm in gemms]}", flush=True)
+    blocks = {gm.name: W.weight_blocks(gm.qtype, gm.w_seed, gm.n, gm.k) for gm in gemms}
+    packed = rz.rz_fp8_pack_weights([(gm.qtype, dev(blocks[gm.name]), gm.n, gm.k, None) for gm in gemms], ws=ws)
+    packed = dict(zip([gm.name for gm in gemms], packed))
+    for grp in groups:
+        x = grp.activation()
+        a8, sc = rz.rz_fp8_quant_act(dev(x), ws=ws)
+        r8, ra, rdq = fp8_path.quant_act(x)
+        ys = rz.rz_fp8_gemm_group(a8, grp.m, sc, [(packed[gm.name][0], packed[gm.name][1]) for gm in grp.gemms])
+        torch.cuda.synchronize()
+        sch = sc.cpu().numpy()
+        assert sch[0] == ra and sch[1] == rdq
+        np.testing.assert_array_equal(a8.cpu().numpy(), r8)
+        sel = np.arange(grp.m) if rows is None else rows(grp)
+        for gm, y in zip(grp.gemms, ys):
+            w8, wsc, wam = packed[gm.name]
+            rw8, rwdq, rwa = fp8_path.pack_weight(gm.qtype, blocks[gm.name], gm.n, gm.k)
+            assert np.float32(wam) == rwa and np.float32(wsc) == rwdq, gm.name
+            np.testing.assert_array_equal(w8.cpu().numpy(), rw8)
+            check_rows(gm.name, y, r8, rw8, rdq, rwdq, sel)
+        del ys
+
+
 def test_config1(rz):
     for grp in W.config_groups(1):
         run_group(rz, grp)
@@ -97,3 +137,18 @@ def test_config3_ffn_full_size(rz):
 def test_config4_layer(rz, layer):
     for grp in W.config_groups(4, layer=layer):
         run_group(rz, grp, rows=_sample_rows(grp.m, seed=grp.act_seed))
+
+
+def test_config3_bench_step(rz):
+    # the FFN step exactly as bench.py launches it: gate, up and down packed in
+    # one call (one launch set), gate and up in one grouped GEMM launch
+    run_step(rz, W.config_groups(3), rows=lambda grp: _sample_rows(grp.m, seed=grp.act_seed + 1))
+
+
+def test_config2_grouped(rz):
+    run_step(rz, W.config_groups(2))
+
+
+def test_config4_layer_grouped(rz):
+    # q+k+v in one launch (288 tiles at M=4096), gate+up in one launch
+    run_step(rz, W.config_groups(4, layer=1), rows=lambda grp: _sample_rows(grp.m, seed=grp.act_seed + 2))
