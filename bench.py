@@ -51,6 +51,8 @@ METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+KGEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kgemv_traffic.json")
+KGEMV_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f) for f in ("kgemv.hip", "rz_device.h")]
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
                   for f in ("gemm.hip", "gemm_common.h", "rz_gemm.h")]
 
@@ -59,23 +61,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per gate/up GEMM launch from the committed counter runs, or
-    None when they are absent or were taken on a different kernel source."""
+def measured_traffic(path=None, sources=None):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    runs, or None when they are absent or were taken on a different kernel
+    source."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path or TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -247,7 +250,15 @@ def small_m(args, dev) -> int:
         q6[str(m)] = {"us": round(t * 1e6, 2), "bytes": b, "gb_s": round(b / t / 1e9, 1),
                       "hbm_frac": round(b / t / 1e12 / HBM_PEAK_TBPS, 4)}
         log(f"q6k down m={m}: {q6[str(m)]}")
+    roof = None
+    if "1" in rows and "kquant_gemv" in rows["1"]:
+        r1 = rows["1"]["kquant_gemv"]
+        roof = {"kernel": "K-quant GEMV at m=1 (N=4608, K=3584, Q4_K), per-call event time over 200 launches",
+                "bound": "hbm", "achieved": r1["gb_s"], "peak": HBM_PEAK_TBPS * 1e3, "unit": "GB/s",
+                "frac": round(r1["gb_s"] / (HBM_PEAK_TBPS * 1e3), 4),
+                "traffic": measured_traffic(KGEMV_TRAFFIC_FILE, KGEMV_SOURCES)}
     out = {"metric": "small-batch matmul at K=3584, N=4608, Q4_K weight (warm)", "unit": "us",
+           "roofline": roof,
            "kquant_gemv_q6k_down_n3584_k18944": q6,
            "higher_is_better": False, "rows": rows, "kquant_bytes": kq_bytes, "data": "synthetic",
            "config": {"workload": "edge configuration: N=4608, K=3584, Q4_K; Student-t(3) activations "
@@ -379,6 +390,13 @@ def main() -> int:
     rz.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration and (args.pack_model or args.gemm_shapes or args.small_m is not None):
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write done")
+        del src, dst
     if args.pack_model:
         return pack_model(args, dev)
     if args.gemm_shapes:
