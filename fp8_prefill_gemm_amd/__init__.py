@@ -51,6 +51,8 @@ _SIGS = {
     "rz_fp8_scales": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_fp8_gemm_plan": (_i32, [_u32, _u32, _u32, _vp]),
     "rz_kquant_gemv": (_i32, [_i32, _vp, _u32, _u32, _vp, _u32, _vp, _vp]),
+    "rz_kquant_weight_scale": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
+    "rz_kquant_fp8_gemm": (_i32, [_vp, _u32, _vp, _i32, _vp, _u32, _u32, _f32, _f32, _vp, _vp]),
     "rz_status_string": (ctypes.c_char_p, [_i32]),
     "rz_last_error_string": (ctypes.c_char_p, []),
     "rz_version": (ctypes.c_char_p, []),
@@ -251,6 +253,32 @@ def rz_kquant_gemv(qtype: int, blocks, n: int, k: int, x, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=blocks.device)
     _check(lib().rz_kquant_gemv(qtype, _ptr(blocks), n, k, _ptr(x), m, _ptr(y), _stream(stream, blocks.device)))
+    return y
+
+
+def rz_kquant_weight_scale(qtype: int, blocks, n: int, k: int, ws=None, stream=None):
+    """-> (w_q, w_dq, w_absmax) of a K-quant weight, without its FP8 codes."""
+    _require_cuda(blocks, ws)
+    dev = blocks.device
+    if ws is None:
+        ws = workspace(dev)
+    q, dq, amax = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    _check(lib().rz_kquant_weight_scale(qtype, _ptr(blocks), n, k, ctypes.addressof(q), ctypes.addressof(dq),
+                                        ctypes.addressof(amax), _ptr(ws), _stream(stream, dev)))
+    return q.value, dq.value, amax.value
+
+
+def rz_kquant_fp8_gemm(a_fp8, m: int, act_scale, qtype: int, blocks, n: int, k: int, w_q: float, w_dq: float,
+                       y=None, stream=None):
+    """-> y fp32 [m][n] = dec(a)[:m] @ dec(E4M3(RN(w * w_q)))^T * act_scale[1] * w_dq,
+    the weight codes made from the K-quant blocks inside the GEMM."""
+    torch = _torch()
+    _require_cuda(a_fp8, act_scale, blocks, y)
+    dev = blocks.device
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    _check(lib().rz_kquant_fp8_gemm(_ptr(a_fp8), m, _ptr(act_scale), qtype, _ptr(blocks), n, k, float(w_q),
+                                    float(w_dq), _ptr(y), _stream(stream, dev)))
     return y
 
 

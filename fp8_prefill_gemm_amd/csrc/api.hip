@@ -162,15 +162,15 @@ static hipError_t wait_for_ticket(const uint32_t* tag, uint32_t ticket, hipStrea
     }
 }
 
-int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
-                       float* w_scale_host, float* w_absmax_host, void* ws, void* stream) {
-    static const char* fn = "rz_fp8_pack_weight";
-    if (!blocks || !w_fp8 || !w_scale_host || !ws) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+// One weight through the pack's two passes; w_fp8 null: scales only.
+// sc receives {a, q, dq}.
+static int pack_one(const char* fn, int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
+                    float sc[3], void* ws, void* stream) {
     if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
     if (int r = check_k(fn, k)) return r;
     if (n == 0) return fail(RZ_ERR_SHAPE, "%s: n must be positive", fn);
     if ((uint64_t)n * k > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: n*k too large", fn);
-    if (!aligned16(blocks) || !aligned16(w_fp8) || !aligned16(ws))
+    if (!aligned16(blocks) || (w_fp8 && !aligned16(w_fp8)) || !aligned16(ws))
         return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     if (int r = check_device(fn)) return r;
     hipStream_t st = as_stream(stream);
@@ -181,19 +181,41 @@ int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, ui
     hipError_t e = rz::launch_pack(qtype, static_cast<const uint8_t*>(blocks), nb, w_fp8,
                                    static_cast<uint8_t*>(ws), slot, ticket, st);
     if (e != hipSuccess) return hip_fail(e, fn);
-    float sc[4];
     if (slot) {
         e = wait_for_ticket(reinterpret_cast<const uint32_t*>(slot) + 3, ticket, st);
         if (e != hipSuccess) return hip_fail(e, fn);
         const volatile float* v = slot;  // written by the device before the ticket
         for (int i = 0; i < 3; ++i) sc[i] = v[i];
     } else {  // no pinned slot: copy the scales back
-        e = hipMemcpyAsync(sc, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof sc,
+        float out[4];
+        e = hipMemcpyAsync(out, static_cast<uint8_t*>(ws) + rz::kWsScaleOffset, sizeof out,
                            hipMemcpyDeviceToHost, st);
         if (e == hipSuccess) e = hipStreamSynchronize(st);
         if (e != hipSuccess) return hip_fail(e, fn);
+        for (int i = 0; i < 3; ++i) sc[i] = out[i];
     }
+    return RZ_OK;
+}
+
+int rz_fp8_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint8_t* w_fp8,
+                       float* w_scale_host, float* w_absmax_host, void* ws, void* stream) {
+    static const char* fn = "rz_fp8_pack_weight";
+    if (!blocks || !w_fp8 || !w_scale_host || !ws) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    float sc[3];
+    if (int r = pack_one(fn, qtype, blocks, n, k, w_fp8, sc, ws, stream)) return r;
     *w_scale_host = sc[2];
+    if (w_absmax_host) *w_absmax_host = sc[0];
+    return RZ_OK;
+}
+
+int rz_kquant_weight_scale(int qtype, const void* blocks, uint32_t n, uint32_t k, float* w_q_host,
+                           float* w_dq_host, float* w_absmax_host, void* ws, void* stream) {
+    static const char* fn = "rz_kquant_weight_scale";
+    if (!blocks || !w_q_host || !w_dq_host || !ws) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    float sc[3];
+    if (int r = pack_one(fn, qtype, blocks, n, k, nullptr, sc, ws, stream)) return r;
+    *w_q_host = sc[1];
+    *w_dq_host = sc[2];
     if (w_absmax_host) *w_absmax_host = sc[0];
     return RZ_OK;
 }
@@ -401,6 +423,27 @@ int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float*
         if (e != hipSuccess) return hip_fail(e, fn);
     }
     return RZ_OK;
+}
+
+int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_dev, int qtype, const void* blocks,
+                       uint32_t n, uint32_t k, float w_q, float w_dq, float* y, void* stream) {
+    static const char* fn = "rz_kquant_fp8_gemm";
+    if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
+    if (int r = check_k(fn, k)) return r;
+    if (k > RZ_MAX_GEMM_K) return fail(RZ_ERR_SHAPE, "%s: k=%u exceeds %u", fn, k, (unsigned)RZ_MAX_GEMM_K);
+    if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
+    if (!a_fp8 || !blocks || !act_scale_dev || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS || (uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS ||
+        (uint64_t)m * n > RZ_MAX_ELEMS || m > 0x7FFFFFF0u || n > 0x7FFFFFF0u)
+        return fail(RZ_ERR_SHAPE, "%s: operand too large", fn);
+    if (!aligned16(a_fp8) || !aligned16(blocks) || !aligned16(y) || ((uintptr_t)act_scale_dev & 3u))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (w_q != w_q || w_q - w_q != 0.0f || w_dq != w_dq || w_dq - w_dq != 0.0f)
+        return fail(RZ_ERR_VALUE, "%s: w_q and w_dq must be finite", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_kquant_fp8_gemm(a_fp8, m, act_scale_dev, qtype, static_cast<const uint8_t*>(blocks), n,
+                                              k, w_q, w_dq, y, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
 size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k) {

@@ -22,40 +22,6 @@ namespace rz {
 namespace {
 using namespace gemm;
 
-// Global -> registers: L x 16 bytes per thread of a [rows][128-byte] K-slice
-// starting at column kb; rows at or past `limit` read as zero.
-template <int L, int NT>
-__device__ __forceinline__ void load_rows(u32x4 (&r)[L], const uint8_t* __restrict__ src, int row0,
-                                          int limit, int K, int kb, int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int idx = tid + i * NT;
-        const int gr = row0 + (idx >> 3);
-        u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-        if (gr < limit) v = *reinterpret_cast<const u32x4*>(src + (size_t)gr * K + kb + ((idx & 7) << 4));
-        r[i] = v;
-    }
-}
-
-// Registers -> one LDS stage (128-byte rows, XOR-swizzled 16-byte chunks).
-template <int L, int NT>
-__device__ __forceinline__ void store_rows(uint8_t* dst, const u32x4 (&r)[L], int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int idx = tid + i * NT;
-        const int row = idx >> 3;
-        *reinterpret_cast<u32x4*>(dst + row * kBK + (((idx & 7) ^ swz(row)) << 4)) = r[i];
-    }
-}
-
-// One 32-byte MFMA operand: row `row`, chunks c0 and c0+1 of a stage.
-__device__ __forceinline__ v8i frag(const uint8_t* base, int row, int c0) {
-    const uint8_t* r = base + row * kBK;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + ((c0 ^ swz(row)) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + (((c0 + 1) ^ swz(row)) << 4));
-    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // Global -> registers for one operand of a stage: thread `tid` moves the
 // 16-byte chunk (tid & 7) of rows (tid >> 3) + (NT/8)*i, i < L.  Buffer loads
 // keep the addressing in one per-lane 32-bit offset (`voff` = (tid >> 3) * K
@@ -196,29 +162,6 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& 
         }
     }
     return true;
-}
-
-// acc * scale -> Y for a TN x TM wave tile whose rows start at m0 and
-// columns at n0.  With the activation as the MFMA A operand, acc[i][j][e]
-// is row m0 + 32j + 8*(e/4) + 4*(lane/32) + e%4, column n0 + 32i + lane%32:
-// a store instruction covers two 128-byte row segments.  Elements outside
-// [0, M) x [0, N) are skipped.
-template <int TN, int TM, int WTN, int WTM>
-__device__ __forceinline__ void store_tile(const v16f (&acc)[TN][TM], float* __restrict__ Y, int M, int N, int m0,
-                                           int n0, int lane, float s) {
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int n = n0 + i * 32 + (lane & 31);
-        if (n >= N) continue;
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m < M) Y[(size_t)m * N + n] = acc[i][j][e] * s;
-            }
-        }
-    }
 }
 
 template <int BN, int BM, int WN, int WM, bool kSplit>

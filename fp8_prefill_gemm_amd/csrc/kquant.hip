@@ -207,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(PackSet P, uint32
 
 // Pass 2 over a set of weights: weight i owns workgroups [g2[i], g2[i+1]).
 // Each workgroup reduces its weight's pass-1 keys, derives the scales and
-// encodes.  The first workgroup of weight i publishes {a, q, dq, 0} to
+// encodes (a weight without an output, w_fp8[i] null, has one workgroup,
+// which only publishes the scales).  The first workgroup of weight i publishes {a, q, dq, 0} to
 // scale_out[4i..] and, when host[i] is given, {a, q, dq} to that coherent
 // host memory followed by ticket[i] in its fourth word, stored with release
 // order at system scope: a host thread that sees the ticket there can read
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(PackSet P, const 
                                __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
+    if (!P.w_fp8[i]) return;  // scales only (one workgroup)
     const bool tensor_finite = sc.a <= 3.402823466e38f;
     const int qt = QT ? QT : P.qtype[i];
     if (qt == 12)
@@ -286,7 +288,7 @@ hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* bl
         P.ticket[i] = ticket ? ticket[i] : 0u;
         P.g1[i + 1] = P.g1[i] + pack_absmax_groups(qtype[i], nb[i]);
         // every encode workgroup re-reduces its weight's keys: keep their number bounded
-        P.g2[i + 1] = P.g2[i] + clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials);
+        P.g2[i + 1] = P.g2[i] + (w_fp8[i] ? clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials) : 1);
         same = same && qtype[i] == qtype[0];
     }
     if (P.g1[count] > kWsPartials) return hipErrorInvalidValue;

@@ -45,6 +45,8 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nblocks
 // uint32, release order) in its fourth word, before the codes.
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nblocks, uint8_t* w_fp8,
                        uint8_t* ws, float* host_scale, uint32_t ticket, hipStream_t st);
+// w_fp8 may be null: then only the scales are computed and published (the
+// pass over the blocks for the absmax, no codes written).
 // Pass-1 workgroups (= partial keys) of one weight.
 int pack_absmax_groups(int qtype, uint64_t nb);
 // The two passes for `count` (<= kMaxPackSet) weights whose pass-1 groups
@@ -54,6 +56,13 @@ int pack_absmax_groups(int qtype, uint64_t nb);
 hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* blocks, const uint64_t* nb,
                            uint8_t* const* w_fp8, uint8_t* ws, float* const* host_scale, const uint32_t* ticket,
                            hipStream_t st);
+
+// ---- kqgemm.hip
+// Y[m][n] = dec(A) * dec(E4M3(RN(w * w_q)))^T * (act_scale[1] * w_dq), the
+// weight codes made from the K-quant blocks inside the GEMM.
+hipError_t launch_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale, int qtype,
+                                  const uint8_t* blocks, uint32_t n, uint32_t k, float w_q, float w_dq, float* y,
+                                  hipStream_t st);
 
 // ---- actquant.hip
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,

@@ -232,6 +232,48 @@ size_t rz_fp8_gemm_workspace_bytes(uint32_t m, uint32_t n, uint32_t k);
 int rz_kquant_gemv(int qtype, const void* blocks, uint32_t n, uint32_t k, const float* x,
                    uint32_t m, float* y, void* stream);
 
+/*
+ * The weight's scale pair without its FP8 codes, for rz_kquant_fp8_gemm
+ * (gemm.rs page, get_or_cache_fp8_weight: per-tensor absmax a of the
+ * dequantised weight, a' = a or 1 when a == 0, q = RN(448/a'),
+ * dq = RN(a'/448)).  One read of the blocks; nothing of size n*k is written.
+ *
+ *   qtype, blocks, n, k, ws, stream   as for rz_fp8_pack_weight
+ *   w_q_host      host out, q (the value the weight is multiplied by before
+ *                 its E4M3 encoding)
+ *   w_dq_host     host out, dq (the value rz_fp8_pack_weight returns as
+ *                 w_scale_host)
+ *   w_absmax_host host out (may be NULL): a
+ * Returns once the scales are on the host (the same pinned-memory handshake
+ * and error behaviour as rz_fp8_pack_weight).
+ */
+int rz_kquant_weight_scale(int qtype, const void* blocks, uint32_t n, uint32_t k, float* w_q_host,
+                           float* w_dq_host, float* w_absmax_host, void* ws, void* stream);
+
+/*
+ * FP8 GEMM straight from the K-quant weight (gemm.rs page,
+ * cublas_prefill_fp8_gemm on the codes get_or_cache_fp8_weight would cache,
+ * made here inside the GEMM so that no FP8 copy of the weight exists):
+ *
+ *   y[i][j] = (sum_kk dec(a_fp8[i][kk]) * dec(E4M3(RN(w[j][kk] * w_q))))
+ *             * act_scale_dev[1] * w_dq                 for i < m, j < n
+ *
+ * where w is the weight decoded exactly as rz_dequant_f32 decodes it.  With
+ * w_q, w_dq from rz_kquant_weight_scale the weight codes are the bytes
+ * rz_fp8_pack_weight writes, so y equals rz_fp8_gemm on the packed weight up
+ * to the order of the fp32 accumulation.
+ *
+ *   a_fp8, m, act_scale_dev   the activation, as for rz_fp8_gemm
+ *   qtype, blocks, n, k       the weight, as for rz_fp8_pack_weight
+ *   w_q, w_dq     host, finite (RZ_ERR_VALUE otherwise)
+ *   y             device out, fp32 [m][n] row-major
+ * k <= RZ_MAX_GEMM_K.  m == 0 or n == 0 is a no-op (any pointer may then be
+ * NULL).  No workspace, no host synchronisation.
+ */
+int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_dev, int qtype,
+                       const void* blocks, uint32_t n, uint32_t k, float w_q, float w_dq, float* y,
+                       void* stream);
+
 /* ---------------------------------------------------------------------
  * Diagnostics: the individual steps, exposed so that each can be checked
  * against the oracle.  Same conventions as above.

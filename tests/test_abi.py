@@ -161,6 +161,45 @@ def test_kquant_gemv_validation(L):
     assert f(12, None, 0, 255, None, 4, None) == RZ_ERR_SHAPE
 
 
+def test_kquant_fp8_gemm_validation(L):
+    def f(a, m, sc, q, b, n, k, wq, wdq, y):
+        return L.rz_kquant_fp8_gemm(a, m, sc, q, b, n, k, wq, wdq, y, None)
+    assert f(None, 4, P3, 12, P2, 8, 256, 1.0, 1.0, P) == RZ_ERR_NULL
+    assert f(P, 4, None, 12, P2, 8, 256, 1.0, 1.0, P) == RZ_ERR_NULL
+    assert f(P, 4, P3, 14, None, 8, 256, 1.0, 1.0, P) == RZ_ERR_NULL
+    assert f(P, 4, P3, 12, P2, 8, 256, 1.0, 1.0, None) == RZ_ERR_NULL
+    assert f(P, 4, P3, 3, P2, 8, 256, 1.0, 1.0, P) == RZ_ERR_QTYPE
+    assert f(P, 4, P3, 12, P2, 8, 300, 1.0, 1.0, P) == RZ_ERR_SHAPE
+    assert f(P, 4, P3, 12, P2, 8, 1 << 24, 1.0, 1.0, P) == RZ_ERR_SHAPE
+    assert f(P, 1 << 20, P3, 12, P2, 1 << 20, 256, 1.0, 1.0, P) == RZ_ERR_SHAPE
+    assert f(BAD, 4, P3, 12, P2, 8, 256, 1.0, 1.0, P) == RZ_ERR_ALIGN
+    assert f(P, 4, P3, 14, BAD, 8, 256, 1.0, 1.0, P) == RZ_ERR_ALIGN
+    assert f(P, 4, P3, 12, P2, 8, 256, 1.0, 1.0, BAD) == RZ_ERR_ALIGN
+    assert f(P, 4, P3, 12, P2, 8, 256, float("nan"), 1.0, P) == RZ_ERR_VALUE
+    assert f(P, 4, P3, 12, P2, 8, 256, 1.0, float("inf"), P) == RZ_ERR_VALUE
+    # empty products are no-ops that touch nothing (no device needed)
+    assert f(None, 0, None, 12, None, 8, 256, 1.0, 1.0, None) == RZ_OK
+    assert f(None, 4, None, 14, None, 0, 256, 1.0, 1.0, None) == RZ_OK
+    assert f(None, 0, None, 12, None, 8, 255, 1.0, 1.0, None) == RZ_ERR_SHAPE
+
+
+def test_kquant_weight_scale_validation(L):
+    q, dq = ctypes.c_float(), ctypes.c_float()
+    aq, adq = ctypes.addressof(q), ctypes.addressof(dq)
+
+    def f(qt, b, n, k, wq, wdq, ws):
+        return L.rz_kquant_weight_scale(qt, b, n, k, wq, wdq, None, ws, None)
+    assert f(12, None, 8, 256, aq, adq, P) == RZ_ERR_NULL
+    assert f(12, P, 8, 256, None, adq, P) == RZ_ERR_NULL
+    assert f(12, P, 8, 256, aq, None, P) == RZ_ERR_NULL
+    assert f(12, P, 8, 256, aq, adq, None) == RZ_ERR_NULL
+    assert f(5, P, 8, 256, aq, adq, P) == RZ_ERR_QTYPE
+    assert f(14, P, 8, 100, aq, adq, P) == RZ_ERR_SHAPE
+    assert f(14, P, 0, 256, aq, adq, P) == RZ_ERR_SHAPE
+    assert f(12, BAD, 8, 256, aq, adq, P) == RZ_ERR_ALIGN
+    assert f(12, P, 8, 256, aq, adq, BAD) == RZ_ERR_ALIGN
+
+
 def test_gemm_group_validation(L):
     V = ctypes.c_void_p
     arr = lambda ct, vals: (ct * len(vals))(*vals)
