@@ -13,20 +13,23 @@
 // pack's bytes exactly (same exact decode, same encoder), so only the
 // accumulation order can differ from the cached path.  This trades the
 // 1 byte per weight cache (and its HBM read) for re-decoding every block
-// once per 128-row activation tile: the decode is vector-ALU work that
-// runs beside the MFMAs of the other workgroup on the CU.
+// once per activation tile: vector-ALU work (about 7 operations per weight)
+// that runs beside the MFMAs of the other waves on the CU.  The decode per
+// product falls with the tile's activation rows, so padded M >= 512 takes
+// 256-row tiles (eight waves, 96 KB of LDS), smaller M 128-row tiles (four
+// waves, 64 KB).
 //
-// Tiles: 128 weight rows x 128 activation rows, four waves of 64 x 64
-// (2 x 2 MFMA 32x32x64 tiles), K-steps of 128 bytes through two LDS stages
-// (the fp8 GEMM's row layout: 128-byte rows, 16-byte chunks XOR-swizzled by
-// row).  While a stage is multiplied, the raw blocks and activation chunks
-// of the next step are in flight in registers; after the MFMAs they are
-// decoded and stored to the other stage.
+// Tiles: 128 weight rows x BM activation rows, waves of 64 x 64 (2 x 2 MFMA
+// 32x32x64 tiles), K-steps of 128 bytes through two LDS stages (the fp8
+// GEMM's row layout: 128-byte rows, 16-byte chunks XOR-swizzled by row).
+// While a stage is multiplied, the raw blocks and activation chunks of the
+// next step are in flight in registers; after the MFMAs they are decoded
+// and stored to the other stage.
 //
-// Thread mapping of a K-step (half h = step & 1 of super-block step / 2):
-//   Q4_K: thread t takes 16-byte quant slice s = 4h + t%4 (32 weights) of
-//         rows t/4 and t/4 + 64, plus each row's 16-byte header;
-//   Q6_K: thread t takes unit (h, l0 = 16 (t%2)) (64 weights) of row t/2.
+// Thread mapping of a K-step (half h = step & 1 of super-block step / 2),
+// rows t/4 + i NT/4 for thread t of NT (each thread 32 weights per row):
+//   Q4_K: 16-byte quant slice s = 4h + t%4, plus the row's 16-byte header;
+//   Q6_K: runs p = t%2 and t%2 + 2 at l0 = 16 ((t/2)%2) (see load_w).
 // Weight rows at or past N are clamped to row N-1 (their products only
 // reach outputs that are never stored); activation rows at or past the
 // padded M read as zero.
@@ -38,45 +41,52 @@ namespace rz {
 namespace {
 using namespace gemm;
 
-constexpr int kNT = 256;
-constexpr int kBN = 128, kBM = 128;  // weight rows, activation rows per tile
+constexpr int kBN = 128;             // weight rows per tile
 constexpr int kWTN = 64, kWTM = 64;  // wave tile
 constexpr int kTN = kWTN / 32, kTM = kWTM / 32;
-constexpr int kLA = kBM * 8 / kNT;   // activation 16-byte chunks per thread and step
 constexpr int kGroupM = 8;           // m-tiles per group in the tile order
-constexpr int kStage = (kBN + kBM) * kBK;
 
-template <int QT>
+// Raw blocks of one K-step for P = 512 / NT weight rows of this thread.
+template <int QT, int P>
 struct RawW;
-template <>
-struct RawW<12> {
-    uint4 head[2], qs[2];
+template <int P>
+struct RawW<12, P> {
+    uint4 head[P], qs[P];
 };
-template <>
-struct RawW<14> {
-    uint4 ql_a, ql_b, qh;
-    uint32_t sc4, dbits;
+template <int P>
+struct RawW<14, P> {
+    uint4 ql[P], qh[P];
+    uint32_t sc2[P], dbits[P];  // sc2: the int8 scales of runs j and j + 2 (bytes 0, 1)
 };
 
-// Raw blocks of K-step kt for this thread's rows.
-template <int QT>
-__device__ __forceinline__ void load_w(RawW<QT>& r, const uint8_t* __restrict__ blocks, int n0, int N, int KB, int kt,
-                                       int tid) {
+// Raw blocks of K-step kt.  Q4_K: thread t takes quant slice s = 4h + t%4
+// of rows t/4 + i NT/4.  Q6_K: thread t takes, of rows t/4 + i NT/4, the
+// runs p = j and j + 2 (j = t%2) at l0 = 16 ((t/2)%2) of half h: their low
+// bits are the low and high nibbles of ql[64h + 32j + l0 ..+16], their high
+// bits bit pairs 2j and 2j + 4 of qh[32h + l0 ..+16], their scales
+// scales[8h + l0/16 + 2p].
+template <int QT, int NT>
+__device__ __forceinline__ void load_w(RawW<QT, 512 / NT>& r, const uint8_t* __restrict__ blocks, int n0, int N,
+                                       int KB, int kt, int tid) {
+    constexpr int P = 512 / NT;
     const int kb = kt >> 1, h = kt & 1;
-    if constexpr (QT == 12) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int row = n0 + (tid >> 2) + 64 * i;
-            row = row < N ? row : N - 1;
+    for (int i = 0; i < P; ++i) {
+        int row = n0 + (tid >> 2) + i * (NT / 4);
+        row = row < N ? row : N - 1;
+        if constexpr (QT == 12) {
             const uint8_t* blk = blocks + ((size_t)row * KB + kb) * kQ4Bytes;
             r.head[i] = *reinterpret_cast<const uint4*>(blk);
             r.qs[i] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (4 * h + (tid & 3)));
+        } else {
+            const uint8_t* blk = blocks + ((size_t)row * KB + kb) * kQ6Bytes;
+            const int j = tid & 1, l0 = 16 * ((tid >> 1) & 1);
+            r.ql[i] = ld16_a2(blk + 64 * h + 32 * j + l0);
+            r.qh[i] = ld16_a2(blk + 128 + 32 * h + l0);
+            const uint8_t* sc = blk + 192 + 8 * h + (l0 >> 4) + 2 * j;
+            r.sc2[i] = (uint32_t)sc[0] | ((uint32_t)sc[4] << 8);
+            r.dbits[i] = *reinterpret_cast<const uint16_t*>(blk + 208);
         }
-    } else {
-        int row = n0 + (tid >> 1);
-        row = row < N ? row : N - 1;
-        const uint8_t* blk = blocks + ((size_t)row * KB + kb) * kQ6Bytes;
-        q6k_load_unit(blk, h, 16 * (tid & 1), r.ql_a, r.ql_b, r.qh, r.sc4, r.dbits);
     }
 }
 
@@ -85,26 +95,44 @@ __device__ __forceinline__ void lds_chunk(uint8_t* stage, int row, int chunk, ui
 }
 
 // Decode + encode the raw blocks into the weight rows of an LDS stage.
-template <int QT>
-__device__ __forceinline__ void store_w(uint8_t* stage, const RawW<QT>& r, int kt, float q, int tid) {
+template <int QT, int NT>
+__device__ __forceinline__ void store_w(uint8_t* stage, const RawW<QT, 512 / NT>& r, int kt, float q, int tid) {
+    constexpr int P = 512 / NT;
     const int h = kt & 1;
-    if constexpr (QT == 12) {
-        const int u = tid & 3;
-        const int c_lo = 4 * (u >> 1) + (u & 1);  // chunk of the low-nibble run; the high one is 2 further
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < P; ++i) {
+        const int row = (tid >> 2) + i * (NT / 4);
+        if constexpr (QT == 12) {
+            const int u = tid & 3;
+            const int c_lo = 4 * (u >> 1) + (u & 1);  // chunk of the low-nibble run; the high one is 2 further
             Q4Unit v;
             q4k_decode_unit(r.head[i], r.qs[i], 4 * h + u, v);
-            const int row = (tid >> 2) + 64 * i;
             lds_chunk(stage, row, c_lo, e4m3_scaled16(v.lo, q));
             lds_chunk(stage, row, c_lo + 2, e4m3_scaled16(v.hi, q));
-        }
-    } else {
-        Q6Unit v;
-        q6k_decode_unit(r.ql_a, r.ql_b, r.qh, r.sc4, r.dbits, v);
-        const int row = tid >> 1, c0 = tid & 1;
+        } else {
+            const int j = tid & 1, c0 = (tid >> 1) & 1;
+            const float d = half_bits_to_float(r.dbits[i]);
+            const float ds0 = d * (float)(int8_t)(r.sc2[i] & 0xFFu);
+            const float ds1 = d * (float)(int8_t)((r.sc2[i] >> 8) & 0xFFu);
+            const uint32_t X[4] = {r.ql[i].x, r.ql[i].y, r.ql[i].z, r.ql[i].w};
+            const uint32_t H[4] = {r.qh[i].x, r.qh[i].y, r.qh[i].z, r.qh[i].w};
+            float v0[16], v1[16];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) lds_chunk(stage, row, 2 * p + c0, e4m3_scaled16(v.v[p], q));
+            for (int w = 0; w < 4; ++w) {
+                uint32_t q0 = (X[w] & 0x0F0F0F0Fu) | (((H[w] >> (2 * j)) & 0x03030303u) << 4);
+                uint32_t q1 = ((X[w] >> 4) & 0x0F0F0F0Fu) | (((H[w] >> (2 * j + 4)) & 0x03030303u) << 4);
+                asm("" : "+v"(q0), "+v"(q1));  // byte b converts with v_cvt_f32_ubyte<b>
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    // (q - 32) is exact and so is ds * (q - 32) (at most 24 bits)
+                    v0[4 * w + b] = ds0 * ((float)((q0 >> (8 * b)) & 0xFFu) - 32.0f);
+                    v1[4 * w + b] = ds1 * ((float)((q1 >> (8 * b)) & 0xFFu) - 32.0f);
+                }
+            }
+            // run p at element 32p + l0 of the half: chunk 2p + l0/16
+            lds_chunk(stage, row, 2 * j + c0, e4m3_scaled16(v0, q));
+            lds_chunk(stage, row, 2 * (j + 2) + c0, e4m3_scaled16(v1, q));
+        }
     }
 }
 
@@ -117,18 +145,22 @@ __device__ __forceinline__ bool tile_of(int w, int T, int& t) {
     return true;
 }
 
-template <int QT>
-__global__ __launch_bounds__(kNT) void kq_fp8_gemm_kernel(const uint8_t* __restrict__ A,
-                                                          const uint8_t* __restrict__ blocks,
-                                                          float* __restrict__ Y, int M, int Mp, int N, int K,
-                                                          const float* __restrict__ act_scale, float w_q,
-                                                          float w_dq, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][kStage];
+// BM activation rows per tile, 2 BM threads: waves 2 (along N) x BM/64.
+template <int QT, int BM>
+__global__ __launch_bounds__(2 * BM) void kq_fp8_gemm_kernel(const uint8_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ blocks,
+                                                             float* __restrict__ Y, int M, int Mp, int N, int K,
+                                                             const float* __restrict__ act_scale, float w_q,
+                                                             float w_dq, int tiles_m, int tiles_n) {
+    constexpr int NT = 2 * BM;
+    constexpr int kLA = BM * 8 / NT;  // activation 16-byte chunks per thread and step
+    constexpr int kStage = (kBN + BM) * kBK;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     int t;
     if (!tile_of(blockIdx.x, tiles_m * tiles_n, t)) return;
     int n0, m0;
-    grouped_origin_bb<kBN, kBM>(t, tiles_m, tiles_n, kGroupM, n0, m0);
+    grouped_origin_bb<kBN, BM>(t, tiles_m, tiles_n, kGroupM, n0, m0);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,22 +174,22 @@ __global__ __launch_bounds__(kNT) void kq_fp8_gemm_kernel(const uint8_t* __restr
 #pragma unroll
         for (int j = 0; j < kTM; ++j) acc[i][j] = (v16f){};
 
-    RawW<QT> rw;
+    RawW<QT, 512 / NT> rw;
     u32x4 ra[kLA];
-    load_w<QT>(rw, blocks, n0, N, KB, 0, tid);
-    load_rows<kLA, kNT>(ra, A, m0, Mp, K, 0, tid);
-    store_w<QT>(smem[0], rw, 0, w_q, tid);
-    store_rows<kLA, kNT>(smem[0] + kBN * kBK, ra, tid);
+    load_w<QT, NT>(rw, blocks, n0, N, KB, 0, tid);
+    load_rows<kLA, NT>(ra, A, m0, Mp, K, 0, tid);
+    store_w<QT, NT>(smem, rw, 0, w_q, tid);
+    store_rows<kLA, NT>(smem + kBN * kBK, ra, tid);
     __syncthreads();
 
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + 1 < KT;
         if (more) {
-            load_w<QT>(rw, blocks, n0, N, KB, kt + 1, tid);
-            load_rows<kLA, kNT>(ra, A, m0, Mp, K, (kt + 1) * kBK, tid);
+            load_w<QT, NT>(rw, blocks, n0, N, KB, kt + 1, tid);
+            load_rows<kLA, NT>(ra, A, m0, Mp, K, (kt + 1) * kBK, tid);
         }
-        const uint8_t* sw = smem[kt & 1];
-        const uint8_t* sa = smem[kt & 1] + kBN * kBK;
+        const uint8_t* sw = smem + (kt & 1) * kStage;
+        const uint8_t* sa = sw + kBN * kBK;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int c0 = kk * 4 + (lane >> 5) * 2;
@@ -174,13 +206,31 @@ __global__ __launch_bounds__(kNT) void kq_fp8_gemm_kernel(const uint8_t* __restr
                                                                                 0, 0, 0, 0);
         }
         if (more) {
-            store_w<QT>(smem[(kt + 1) & 1], rw, kt + 1, w_q, tid);
-            store_rows<kLA, kNT>(smem[(kt + 1) & 1] + kBN * kBK, ra, tid);
+            uint8_t* nx = smem + ((kt + 1) & 1) * kStage;
+            store_w<QT, NT>(nx, rw, kt + 1, w_q, tid);
+            store_rows<kLA, NT>(nx + kBN * kBK, ra, tid);
         }
         __syncthreads();
     }
 
     store_tile<kTN, kTM, kWTN, kWTM>(acc, Y, M, N, m0 + wm * kWTM, n0 + wn * kWTN, lane, act_scale[1] * w_dq);
+}
+
+template <int QT, int BM>
+hipError_t launch_bm(const uint8_t* a_fp8, int m, int mp, const float* act_scale, const uint8_t* blocks, int n, int k,
+                     float w_q, float w_dq, float* y, hipStream_t st) {
+    constexpr int lds = 2 * (kBN + BM) * kBK;
+    const int tiles_m = (mp + BM - 1) / BM, tiles_n = (n + kBN - 1) / kBN;
+    const int T = tiles_m * tiles_n;
+    const int grid = (T + kXcds - 1) / kXcds * kXcds;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kq_fp8_gemm_kernel<QT, BM>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+    }
+    kq_fp8_gemm_kernel<QT, BM><<<grid, 2 * BM, lds, st>>>(a_fp8, blocks, y, m, mp, n, k, act_scale, w_q, w_dq,
+                                                          tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -189,16 +239,14 @@ hipError_t launch_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float*
                                   const uint8_t* blocks, uint32_t n, uint32_t k, float w_q, float w_dq, float* y,
                                   hipStream_t st) {
     const int mp = (int)((m + 15u) & ~15u);
-    const int tiles_m = (mp + kBM - 1) / kBM, tiles_n = ((int)n + kBN - 1) / kBN;
-    const int T = tiles_m * tiles_n;
-    const int grid = (T + kXcds - 1) / kXcds * kXcds;
+    // 256-row activation tiles halve the decode work per product; below 512
+    // rows they would leave too many rows of their tiles empty
+    const bool wide = mp >= 512;
     if (qtype == 12)
-        kq_fp8_gemm_kernel<12><<<grid, kNT, 0, st>>>(a_fp8, blocks, y, (int)m, mp, (int)n, (int)k, act_scale, w_q,
-                                                      w_dq, tiles_m, tiles_n);
-    else
-        kq_fp8_gemm_kernel<14><<<grid, kNT, 0, st>>>(a_fp8, blocks, y, (int)m, mp, (int)n, (int)k, act_scale, w_q,
-                                                      w_dq, tiles_m, tiles_n);
-    return hipGetLastError();
+        return wide ? launch_bm<12, 256>(a_fp8, (int)m, mp, act_scale, blocks, (int)n, (int)k, w_q, w_dq, y, st)
+                    : launch_bm<12, 128>(a_fp8, (int)m, mp, act_scale, blocks, (int)n, (int)k, w_q, w_dq, y, st);
+    return wide ? launch_bm<14, 256>(a_fp8, (int)m, mp, act_scale, blocks, (int)n, (int)k, w_q, w_dq, y, st)
+                : launch_bm<14, 128>(a_fp8, (int)m, mp, act_scale, blocks, (int)n, (int)k, w_q, w_dq, y, st);
 }
 
 }  // namespace rz
