@@ -94,7 +94,63 @@ __device__ __forceinline__ void lds_chunk(uint8_t* stage, int row, int chunk, ui
     *reinterpret_cast<uint4*>(stage + row * kBK + ((chunk ^ swz(row)) << 4)) = v;
 }
 
+// Codes of RN(v[i] * q), i < 16, for finite v[i] (and the finite q the
+// entry point checks): a product may overflow to +-Inf but is never NaN, so
+// the converter only needs the clamp to +-448 and the flush below 2^-6 (the
+// same codes e4m3_scaled16 gives for such inputs).
+__device__ __forceinline__ uint4 encode16_no_nan(const float v[16], float q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float p = v[4 * i + b] * q;
+            const float t = __builtin_amdgcn_fmed3f(p, -kFp8Max, kFp8Max);
+            y[b] = (fabsf(p) < 0.015625f) ? 0.0f : t;
+        }
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+    }
+    return (uint4){w[0], w[1], w[2], w[3]};
+}
+
+template <bool kFin>
+__device__ __forceinline__ uint4 encode16(const float v[16], float q) {
+    if constexpr (kFin)
+        return encode16_no_nan(v, q);
+    else
+        return e4m3_scaled16(v, q);
+}
+
+// Q6_K runs p = j and j + 2 of a half-unit: 16 values each.  kFin: d is
+// finite, so ds * (q - 32), which is exact (at most 23 significant bits),
+// is formed as one fused multiply-add ds * q - 32 ds.
+template <bool kFin>
+__device__ __forceinline__ void q6k_decode_half(uint4 ql, uint4 qh, int j, uint32_t sc2, uint32_t dbits,
+                                                float (&v0)[16], float (&v1)[16]) {
+    const float d = half_bits_to_float(dbits);
+    const float ds0 = d * (float)(int8_t)(sc2 & 0xFFu);
+    const float ds1 = d * (float)(int8_t)((sc2 >> 8) & 0xFFu);
+    const uint32_t X[4] = {ql.x, ql.y, ql.z, ql.w};
+    const uint32_t H[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t q0 = (X[w] & 0x0F0F0F0Fu) | (((H[w] >> (2 * j)) & 0x03030303u) << 4);
+        uint32_t q1 = ((X[w] >> 4) & 0x0F0F0F0Fu) | (((H[w] >> (2 * j + 4)) & 0x03030303u) << 4);
+        asm("" : "+v"(q0), "+v"(q1));  // byte b converts with v_cvt_f32_ubyte<b>
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float f0 = (float)((q0 >> (8 * b)) & 0xFFu), f1 = (float)((q1 >> (8 * b)) & 0xFFu);
+            v0[4 * w + b] = kFin ? __builtin_fmaf(ds0, f0, -32.0f * ds0) : ds0 * (f0 - 32.0f);
+            v1[4 * w + b] = kFin ? __builtin_fmaf(ds1, f1, -32.0f * ds1) : ds1 * (f1 - 32.0f);
+        }
+    }
+}
+
 // Decode + encode the raw blocks into the weight rows of an LDS stage.
+// Waves whose blocks all have finite f16 scales take the encoder without
+// NaN handling (the decoded values are then finite).
 template <int QT, int NT>
 __device__ __forceinline__ void store_w(uint8_t* stage, const RawW<QT, 512 / NT>& r, int kt, float q, int tid) {
     constexpr int P = 512 / NT;
@@ -107,31 +163,26 @@ __device__ __forceinline__ void store_w(uint8_t* stage, const RawW<QT, 512 / NT>
             const int c_lo = 4 * (u >> 1) + (u & 1);  // chunk of the low-nibble run; the high one is 2 further
             Q4Unit v;
             q4k_decode_unit(r.head[i], r.qs[i], 4 * h + u, v);
-            lds_chunk(stage, row, c_lo, e4m3_scaled16(v.lo, q));
-            lds_chunk(stage, row, c_lo + 2, e4m3_scaled16(v.hi, q));
+            if (__all(half_finite(r.head[i].x) && half_finite(r.head[i].x >> 16))) {
+                lds_chunk(stage, row, c_lo, encode16<true>(v.lo, q));
+                lds_chunk(stage, row, c_lo + 2, encode16<true>(v.hi, q));
+            } else {
+                lds_chunk(stage, row, c_lo, encode16<false>(v.lo, q));
+                lds_chunk(stage, row, c_lo + 2, encode16<false>(v.hi, q));
+            }
         } else {
             const int j = tid & 1, c0 = (tid >> 1) & 1;
-            const float d = half_bits_to_float(r.dbits[i]);
-            const float ds0 = d * (float)(int8_t)(r.sc2[i] & 0xFFu);
-            const float ds1 = d * (float)(int8_t)((r.sc2[i] >> 8) & 0xFFu);
-            const uint32_t X[4] = {r.ql[i].x, r.ql[i].y, r.ql[i].z, r.ql[i].w};
-            const uint32_t H[4] = {r.qh[i].x, r.qh[i].y, r.qh[i].z, r.qh[i].w};
             float v0[16], v1[16];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint32_t q0 = (X[w] & 0x0F0F0F0Fu) | (((H[w] >> (2 * j)) & 0x03030303u) << 4);
-                uint32_t q1 = ((X[w] >> 4) & 0x0F0F0F0Fu) | (((H[w] >> (2 * j + 4)) & 0x03030303u) << 4);
-                asm("" : "+v"(q0), "+v"(q1));  // byte b converts with v_cvt_f32_ubyte<b>
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    // (q - 32) is exact and so is ds * (q - 32) (at most 24 bits)
-                    v0[4 * w + b] = ds0 * ((float)((q0 >> (8 * b)) & 0xFFu) - 32.0f);
-                    v1[4 * w + b] = ds1 * ((float)((q1 >> (8 * b)) & 0xFFu) - 32.0f);
-                }
-            }
             // run p at element 32p + l0 of the half: chunk 2p + l0/16
-            lds_chunk(stage, row, 2 * j + c0, e4m3_scaled16(v0, q));
-            lds_chunk(stage, row, 2 * (j + 2) + c0, e4m3_scaled16(v1, q));
+            if (__all(half_finite(r.dbits[i]))) {
+                q6k_decode_half<true>(r.ql[i], r.qh[i], j, r.sc2[i], r.dbits[i], v0, v1);
+                lds_chunk(stage, row, 2 * j + c0, encode16<true>(v0, q));
+                lds_chunk(stage, row, 2 * (j + 2) + c0, encode16<true>(v1, q));
+            } else {
+                q6k_decode_half<false>(r.ql[i], r.qh[i], j, r.sc2[i], r.dbits[i], v0, v1);
+                lds_chunk(stage, row, 2 * j + c0, encode16<false>(v0, q));
+                lds_chunk(stage, row, 2 * (j + 2) + c0, encode16<false>(v1, q));
+            }
         }
     }
 }

@@ -116,6 +116,25 @@ def test_matches_cached_path(rz, qtype):
     check(y, a8h, w8, m, dqa, dqw)
 
 
+@pytest.mark.parametrize("qtype", [W.Q4_K, W.Q6_K])
+def test_nan_block_scale(rz, qtype):
+    # a few blocks with an f16 NaN super-block scale: their weights decode to
+    # NaN, which the absmax ignores and the encoder maps to 0x7E (448); the
+    # waves that hold them take the encoder with NaN handling, the others
+    # the one without
+    m, n, k = 520, 300, 768
+    blocks = W.weight_blocks(qtype, 8450 + qtype, n, k)
+    bb = 144 if qtype == W.Q4_K else 210
+    off = 0 if qtype == W.Q4_K else 208
+    view = blocks.reshape(-1, bb)
+    for b in (0, 7, 3 * (k // 256) + 1, view.shape[0] - 1):
+        view[b, off:off + 2] = (0x00, 0x7E)  # f16 NaN, little-endian
+    x = W.act_normal(8451, m, k)
+    y, a8, w8, dqa, dqw, _ = run(rz, qtype, blocks, n, k, x)
+    assert (w8 == 0x7E).any()
+    check(y, a8, w8, m, dqa, dqw)
+
+
 def test_zero_activation_gives_exact_zero(rz):
     m, n, k = 40, 300, 512
     for qtype in (W.Q4_K, W.Q6_K):
