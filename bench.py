@@ -33,6 +33,10 @@ shapes (warm, random E4M3 codes) and the 28-layer M=4096 sweep from them.
 
 --small-m instead times the small-batch routes (GEMV straight from K-quant
 blocks, FP8 GEMM, activation quantisation + FP8 GEMM) at N=4608, K=3584.
+
+--kquant-gemm instead times the FP8 GEMM that encodes the weight from its
+K-quant blocks inside the kernel (no FP8 weight cache) beside the cached
+path's GEMM, at the model's prefill shapes (warm).
 """
 from __future__ import annotations
 
@@ -353,6 +357,69 @@ def gemm_shapes(args, dev) -> int:
     return 0
 
 
+def kquant_gemm(args, dev) -> int:
+    """Warm time of the FP8 GEMM that makes the weight codes from the K-quant
+    blocks in the kernel (rz_kquant_fp8_gemm), beside the cached path's GEMM
+    on the packed weight (rz_fp8_gemm), per prefill shape of the 7B-class
+    model (one line): seeded K-quant blocks and activations, HIP events
+    around 20 launches after 5 warm-up launches.  Also the one-pass weight
+    scale (rz_kquant_weight_scale, including its host wait) and the weight
+    bytes each path keeps resident for the 28-layer model."""
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    H, KV, F, L = 3584, 512, 18944, 28
+    shapes = [("cfg2 q", 512, W.Q4_K, H, H), ("cfg3 gate/up", 2048, W.Q4_K, F, H),
+              ("cfg3 down", 2048, W.Q6_K, H, F), ("cfg4 q/o", 4096, W.Q4_K, H, H),
+              ("cfg4 k/v", 4096, W.Q4_K, KV, H), ("cfg4 gate/up", 4096, W.Q4_K, F, H),
+              ("cfg4 down", 4096, W.Q6_K, H, F)]
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=20):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    rows = {}
+    for name, m, qt, n, k in shapes:
+        blocks = torch.from_numpy(W.weight_blocks(qt, 31 + n, n, k)).to(dev)
+        a8, sc = rz.rz_fp8_quant_act(torch.from_numpy(W.act_student_t(32 + m, m, k)).to(dev), stream=stream)
+        q, dq, _ = rz.rz_kquant_weight_scale(qt, blocks, n, k, stream=stream)
+        w8, scale, _ = rz.rz_fp8_pack_weight(qt, blocks, n, k, stream=stream)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        tf = timed(lambda: rz.rz_kquant_fp8_gemm(a8, m, sc, qt, blocks, n, k, q, dq, y, stream))
+        tc = timed(lambda: rz.rz_fp8_gemm(a8, w8, m, sc, scale, y, stream))
+        t0 = time.perf_counter()
+        for _ in range(5):
+            rz.rz_kquant_weight_scale(qt, blocks, n, k, stream=stream)
+        ts = (time.perf_counter() - t0) / 5
+        fl = 2.0 * m * n * k
+        rows[name] = {"m": m, "n": n, "k": k, "qtype": "Q4_K" if qt == W.Q4_K else "Q6_K",
+                      "fused_us": round(tf * 1e6, 1), "fused_tflops": round(fl / tf / 1e12, 1),
+                      "cached_us": round(tc * 1e6, 1), "cached_tflops": round(fl / tc / 1e12, 1),
+                      "weight_scale_us": round(ts * 1e6, 1)}
+        log(f"{name}: {rows[name]}")
+        del blocks, a8, w8, y
+    per_layer = {"q/o": (2, W.Q4_K, H, H), "k/v": (2, W.Q4_K, KV, H), "gate/up": (2, W.Q4_K, F, H),
+                 "down": (1, W.Q6_K, H, F)}
+    kq = sum(c * rz.rz_weight_bytes(qt, n, k) for c, qt, n, k in per_layer.values()) * L
+    f8 = sum(c * n * k for c, _, n, k in per_layer.values()) * L
+    out = {"metric": "FP8 GEMM from K-quant blocks vs cached FP8 weight (warm)", "unit": "us",
+           "higher_is_better": False, "rows": rows,
+           "resident_weight_bytes_28_layers": {"kquant_only": kq, "kquant_plus_fp8_cache": kq + f8},
+           "data": "synthetic", "config": {"workload": "prefill GEMM shapes of the 7B-class model"}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +436,8 @@ def main() -> int:
                     help="instead time the FP8 GEMM alone at every configuration's shapes (warm)")
     ap.add_argument("--small-m", type=int, nargs="*", default=None,
                     help="instead time the small-batch paths at N=4608, K=3584 (Q4_K) for these m")
+    ap.add_argument("--kquant-gemm", action="store_true",
+                    help="instead time the GEMM straight from K-quant blocks beside the cached path (warm)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -401,6 +470,8 @@ def main() -> int:
         return pack_model(args, dev)
     if args.gemm_shapes:
         return gemm_shapes(args, dev)
+    if args.kquant_gemm:
+        return kquant_gemm(args, dev)
     if args.small_m is not None:
         if not args.small_m:
             args.small_m = [1, 2, 3, 4, 8, 37]
