@@ -51,6 +51,7 @@ _SIGS = {
     "rz_fp8_scales": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_fp8_gemm_plan": (_i32, [_u32, _u32, _u32, _vp]),
     "rz_kquant_gemv": (_i32, [_i32, _vp, _u32, _u32, _vp, _u32, _vp, _vp]),
+    "rz_route_kquant_gemv": (_i32, [_u32]),
     "rz_kquant_weight_scale": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "rz_kquant_fp8_gemm": (_i32, [_vp, _u32, _vp, _i32, _vp, _u32, _u32, _f32, _f32, _vp, _vp]),
     "rz_status_string": (ctypes.c_char_p, [_i32]),
@@ -254,6 +255,12 @@ def rz_kquant_gemv(qtype: int, blocks, n: int, k: int, x, y=None, stream=None):
         y = torch.empty((m, n), dtype=torch.float32, device=blocks.device)
     _check(lib().rz_kquant_gemv(qtype, _ptr(blocks), n, k, _ptr(x), m, _ptr(y), _stream(stream, blocks.device)))
     return y
+
+
+def rz_route_kquant_gemv(m: int) -> bool:
+    """True when a batch of m rows should take rz_kquant_gemv rather than the
+    FP8 path (activation quantisation + FP8 GEMM)."""
+    return bool(lib().rz_route_kquant_gemv(m))
 
 
 def rz_kquant_weight_scale(qtype: int, blocks, n: int, k: int, ws=None, stream=None):

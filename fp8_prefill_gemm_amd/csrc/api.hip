@@ -425,6 +425,8 @@ int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float*
     return RZ_OK;
 }
 
+int rz_route_kquant_gemv(uint32_t m) { return m >= 1u && m <= RZ_KGEMV_ROUTE_MAX_M ? 1 : 0; }
+
 int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_dev, int qtype, const void* blocks,
                        uint32_t n, uint32_t k, float w_q, float w_dq, float* y, void* stream) {
     static const char* fn = "rz_kquant_fp8_gemm";

@@ -183,6 +183,12 @@ def test_kquant_fp8_gemm_validation(L):
     assert f(None, 0, None, 12, None, 8, 255, 1.0, 1.0, None) == RZ_ERR_SHAPE
 
 
+def test_route_kquant_gemv(L):
+    # GEMV route for 1..4 rows, the FP8 path above; host only
+    assert [L.rz_route_kquant_gemv(m) for m in (0, 1, 2, 3, 4, 5, 8, 16, 2048)] == [0, 1, 1, 1, 1, 0, 0, 0, 0]
+    assert [rz.rz_route_kquant_gemv(m) for m in (1, 4, 5)] == [True, True, False]
+
+
 def test_kquant_weight_scale_validation(L):
     q, dq = ctypes.c_float(), ctypes.c_float()
     aq, adq = ctypes.addressof(q), ctypes.addressof(dq)
