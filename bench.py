@@ -412,8 +412,13 @@ def kquant_gemm(args, dev) -> int:
                  "down": (1, W.Q6_K, H, F)}
     kq = sum(c * rz.rz_weight_bytes(qt, n, k) for c, qt, n, k in per_layer.values()) * L
     f8 = sum(c * n * k for c, _, n, k in per_layer.values()) * L
+    g = rows["cfg3 gate/up"]
+    ach = 2.0 * g["m"] * g["n"] * g["k"] / (g["fused_us"] * 1e-6) / 1e12
+    roof = {"kernel": "kq_fp8_gemm_kernel<Q4_K, 256-row tiles> (M=2048, N=18944, K=3584)", "bound": "mfma",
+            "achieved": round(ach, 1), "peak": 5000.0, "unit": "TFLOP/s", "frac": round(ach / 5000.0, 4),
+            "traffic": None}
     out = {"metric": "FP8 GEMM from K-quant blocks vs cached FP8 weight (warm)", "unit": "us",
-           "higher_is_better": False, "rows": rows,
+           "higher_is_better": False, "rows": rows, "roofline": roof,
            "resident_weight_bytes_28_layers": {"kquant_only": kq, "kquant_plus_fp8_cache": kq + f8},
            "data": "synthetic", "config": {"workload": "prefill GEMM shapes of the 7B-class model"}}
     print(json.dumps(out), flush=True)
