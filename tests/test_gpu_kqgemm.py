@@ -86,11 +86,12 @@ def test_weight_scale_zero_weight(rz):
 
 # several tiles in both directions with ragged tails (n and m not multiples
 # of 128, m not a multiple of 16), one and several super-blocks; padded
-# m >= 512 takes the 256-row tiles, smaller m the 128-row tiles
+# m >= 512 takes the 256-row tiles (1000 x 4100: 4 x 33 of them, ragged in
+# both directions), smaller m the 128-row tiles
 @pytest.mark.parametrize("qtype", [W.Q4_K, W.Q6_K])
 @pytest.mark.parametrize("m,n,k", [(16, 256, 512), (1, 64, 256), (37, 200, 768), (130, 129, 512),
                                    (300, 520, 1024), (257, 384, 2304), (600, 1000, 512),
-                                   (1000, 520, 768), (496, 260, 256)])
+                                   (1000, 520, 768), (496, 260, 256), (1000, 4100, 256)])
 def test_parity_shapes(rz, qtype, m, n, k):
     blocks = W.weight_blocks(qtype, 8200 + n + m, n, k)
     x = W.act_student_t(8300 + m + k, m, k)
