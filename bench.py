@@ -93,10 +93,12 @@ def cpu_baseline(x_ffn, x_down, gate_blocks, down_blocks, gate, dn, m_rows=128):
     down GEMMs."""
     import numpy as np
     try:
-        threads = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = max(1, min(threads, 16))
+        host_cores = os.cpu_count() or 1
+    # the GPU box's CPU share is 16 threads per GPU whatever the affinity
+    # mask shows; BLAS gets all of that share
+    threads = max(1, min(host_cores, 16))
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=threads, user_api="blas")
@@ -125,12 +127,14 @@ def cpu_baseline(x_ffn, x_down, gate_blocks, down_blocks, gate, dn, m_rows=128):
         "value": flops / total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cores": host_cores,
         "kind": "oracle",
         "sample": (f"oracle (numpy) on a slice of the same step: pack the full {gate.n}x{gate.k} Q4_K gate "
                    f"weight ({t[1] - t[0]:.2f}s) and {dn.n}x{dn.k} Q6_K down weight ({t[2] - t[1]:.2f}s), "
                    f"quantise both full inputs ({t[3] - t[2]:.2f}s), exact gate and down GEMMs for {m_rows} of "
                    f"{x_ffn.shape[0]} output rows ({t[4] - t[3]:.2f}s); value = those rows' 2*m*N*K FLOPs / "
-                   f"total time ({total:.1f}s); cores = BLAS threads"),
+                   f"total time ({total:.1f}s); cores = BLAS threads = the box's CPU share per GPU "
+                   f"(16), of {host_cores} cores in the affinity mask"),
     }
 
 

@@ -99,11 +99,27 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream, device):
+def _torch_stream(stream, device):
+    """The torch stream a call runs on: `stream`, or the device's current one."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _stream(stream, device):
+    return ctypes.c_void_p(_torch_stream(stream, device).cuda_stream)
+
+
+def _empty(shape, dtype, device, stream=None):
+    """A new device tensor allocated on the call's stream.
+
+    The caching allocator ties a block to the stream it was allocated on:
+    once the tensor is freed, the block is reused only by work ordered after
+    what that stream has queued, so a temporary freed when a call returns
+    (a workspace, an output the caller drops) is never handed to a new
+    allocation while the call's kernels still use it."""
+    torch = _torch()
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _require_cuda(*tensors):
@@ -112,10 +128,11 @@ def _require_cuda(*tensors):
             raise ValueError("rz_fp8 works on device (cuda/hip) tensors only")
 
 
-def workspace(device) -> "torch.Tensor":
-    """A fresh device workspace of rz_workspace_bytes() bytes."""
+def workspace(device, stream=None) -> "torch.Tensor":
+    """A fresh device workspace of rz_workspace_bytes() bytes, allocated on
+    `stream` (default: the device's current stream)."""
     torch = _torch()
-    return torch.empty(lib().rz_workspace_bytes(), dtype=torch.uint8, device=device)
+    return _empty(lib().rz_workspace_bytes(), torch.uint8, device, stream)
 
 
 def rz_pad_m(m: int) -> int:
@@ -145,9 +162,9 @@ def rz_fp8_pack_weight(qtype: int, blocks, n: int, k: int, w_fp8=None, ws=None, 
     _require_cuda(blocks, w_fp8, ws)
     dev = blocks.device
     if w_fp8 is None:
-        w_fp8 = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        w_fp8 = _empty((n, k), torch.uint8, dev, stream)
     if ws is None:
-        ws = workspace(dev)
+        ws = workspace(dev, stream)
     scale = ctypes.c_float()
     amax = ctypes.c_float()
     _check(lib().rz_fp8_pack_weight(qtype, _ptr(blocks), n, k, _ptr(w_fp8), ctypes.addressof(scale),
@@ -167,9 +184,9 @@ def rz_fp8_pack_weights(weights, ws=None, stream=None):
     outs = []
     for q, b, n, k, w8 in weights:
         _require_cuda(b, w8)
-        outs.append(torch.empty((n, k), dtype=torch.uint8, device=b.device) if w8 is None else w8)
+        outs.append(_empty((n, k), torch.uint8, b.device, stream) if w8 is None else w8)
     if ws is None:
-        ws = workspace(dev)
+        ws = workspace(dev, stream)
     _require_cuda(ws)
     qt = (ctypes.c_int * cnt)(*[w[0] for w in weights])
     bp = (ctypes.c_void_p * cnt)(*[_ptr(w[1]) for w in weights])
@@ -191,11 +208,11 @@ def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
     m, k = x.shape
     dev = x.device
     if a_fp8 is None:
-        a_fp8 = torch.empty((rz_pad_m(m), k), dtype=torch.uint8, device=dev)
+        a_fp8 = _empty((rz_pad_m(m), k), torch.uint8, dev, stream)
     if act_scale is None:
-        act_scale = torch.empty(4, dtype=torch.float32, device=dev)
+        act_scale = _empty(4, torch.float32, dev, stream)
     if ws is None:
-        ws = workspace(dev)
+        ws = workspace(dev, stream)
     _check(lib().rz_fp8_quant_act(_ptr(x), m, k, _ptr(a_fp8), _ptr(act_scale), _ptr(ws),
                                   _stream(stream, dev)))
     return a_fp8, act_scale
@@ -204,16 +221,23 @@ def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
 _gemm_ws = {}
 
 
-def gemm_workspace(device, nbytes: int):
-    """A zero-filled GEMM workspace of at least `nbytes`, cached per device.
+def gemm_workspace(device, nbytes: int, stream=None):
+    """A zero-filled GEMM workspace of at least `nbytes`, cached per (device,
+    stream).
 
     The GEMM returns its workspace to the zero state, so one buffer serves
-    every call issued in order on one stream."""
+    every call issued in order on one stream; calls on different streams
+    must not share one (their split-K counters and partial sums would race),
+    so each stream gets its own.  The buffer is allocated and zero-filled on
+    that stream, so the fill is ordered before the stream's GEMMs."""
     torch = _torch()
-    key = torch.device(device).index or 0
+    dev = torch.device(device)
+    st = _torch_stream(stream, dev)
+    key = (dev.index or 0, st.cuda_stream)
     buf = _gemm_ws.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(st):
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _gemm_ws[key] = buf
     return buf
 
@@ -232,10 +256,10 @@ def rz_fp8_gemm(a_fp8, w_fp8, m: int, act_scale, w_scale: float, y=None, stream=
     n, k = w_fp8.shape
     dev = w_fp8.device
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        y = _empty((m, n), torch.float32, dev, stream)
     if isinstance(ws, str):
         need = rz_fp8_gemm_workspace_bytes(m, n, k)
-        ws = gemm_workspace(dev, need) if need else None
+        ws = gemm_workspace(dev, need, stream) if need else None
     _require_cuda(ws)
     _check(lib().rz_fp8_gemm(_ptr(a_fp8), _ptr(w_fp8), m, n, k, _ptr(act_scale), float(w_scale),
                              _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, dev)))
@@ -252,7 +276,7 @@ def rz_kquant_gemv(qtype: int, blocks, n: int, k: int, x, y=None, stream=None):
     _require_cuda(blocks, x, y)
     m = x.shape[0]
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=blocks.device)
+        y = _empty((m, n), torch.float32, blocks.device, stream)
     _check(lib().rz_kquant_gemv(qtype, _ptr(blocks), n, k, _ptr(x), m, _ptr(y), _stream(stream, blocks.device)))
     return y
 
@@ -268,7 +292,7 @@ def rz_kquant_weight_scale(qtype: int, blocks, n: int, k: int, ws=None, stream=N
     _require_cuda(blocks, ws)
     dev = blocks.device
     if ws is None:
-        ws = workspace(dev)
+        ws = workspace(dev, stream)
     q, dq, amax = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
     _check(lib().rz_kquant_weight_scale(qtype, _ptr(blocks), n, k, ctypes.addressof(q), ctypes.addressof(dq),
                                         ctypes.addressof(amax), _ptr(ws), _stream(stream, dev)))
@@ -283,7 +307,7 @@ def rz_kquant_fp8_gemm(a_fp8, m: int, act_scale, qtype: int, blocks, n: int, k: 
     _require_cuda(a_fp8, act_scale, blocks, y)
     dev = blocks.device
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        y = _empty((m, n), torch.float32, dev, stream)
     _check(lib().rz_kquant_fp8_gemm(_ptr(a_fp8), m, _ptr(act_scale), qtype, _ptr(blocks), n, k, float(w_q),
                                     float(w_dq), _ptr(y), _stream(stream, dev)))
     return y
@@ -300,11 +324,11 @@ def rz_fp8_gemm_group(a_fp8, m: int, act_scale, weights, ys=None, stream=None, w
     k = a_fp8.shape[1]
     dev = a_fp8.device
     if ys is None:
-        ys = [torch.empty((m, w.shape[0]), dtype=torch.float32, device=dev) for w, _ in weights]
+        ys = [_empty((m, w.shape[0]), torch.float32, dev, stream) for w, _ in weights]
     _require_cuda(*ys)
     if isinstance(ws, str):
         need = max([rz_fp8_gemm_workspace_bytes(m, w.shape[0], k) for w, _ in weights] + [0])
-        ws = gemm_workspace(dev, need) if need else None
+        ws = gemm_workspace(dev, need, stream) if need else None
     _require_cuda(ws)
     wp = (ctypes.c_void_p * max(cnt, 1))(*[_ptr(w) for w, _ in weights])
     nn = (ctypes.c_uint32 * max(cnt, 1))(*[w.shape[0] for w, _ in weights])
@@ -320,7 +344,7 @@ def rz_dequant_f32(qtype: int, blocks, n: int, k: int, out=None, stream=None):
     torch = _torch()
     _require_cuda(blocks, out)
     if out is None:
-        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
+        out = _empty((n, k), torch.float32, blocks.device, stream)
     _check(lib().rz_dequant_f32(qtype, _ptr(blocks), n, k, _ptr(out), _stream(stream, blocks.device)))
     return out
 
@@ -329,9 +353,9 @@ def rz_absmax_f32(x, out=None, ws=None, stream=None):
     torch = _torch()
     _require_cuda(x, out, ws)
     if out is None:
-        out = torch.empty(4, dtype=torch.float32, device=x.device)
+        out = _empty(4, torch.float32, x.device, stream)
     if ws is None:
-        ws = workspace(x.device)
+        ws = workspace(x.device, stream)
     _check(lib().rz_absmax_f32(_ptr(x), x.numel(), _ptr(out), _ptr(ws), _stream(stream, x.device)))
     return out
 
@@ -340,7 +364,7 @@ def rz_e4m3_encode(x, scale: float, out=None, stream=None):
     torch = _torch()
     _require_cuda(x, out)
     if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        out = _empty(x.shape, torch.uint8, x.device, stream)
     _check(lib().rz_e4m3_encode(_ptr(x), x.numel(), float(scale), _ptr(out), _stream(stream, x.device)))
     return out
 
@@ -349,9 +373,9 @@ def rz_fp8_scales(absmax, q=None, dq=None, stream=None):
     torch = _torch()
     _require_cuda(absmax, q, dq)
     if q is None:
-        q = torch.empty_like(absmax)
+        q = _empty(absmax.shape, absmax.dtype, absmax.device, stream)
     if dq is None:
-        dq = torch.empty_like(absmax)
+        dq = _empty(absmax.shape, absmax.dtype, absmax.device, stream)
     _check(lib().rz_fp8_scales(_ptr(absmax), absmax.numel(), _ptr(q), _ptr(dq),
                                _stream(stream, absmax.device)))
     return q, dq

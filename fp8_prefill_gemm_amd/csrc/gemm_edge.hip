@@ -130,11 +130,17 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& 
             for (int g = 0; g < 4; ++g)
                 mine[((i * TM + j) * 4 + g) * NT + tid] =
                     make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-    // all chunks of this tile run on this XCD, whose L2 is coherent for its
-    // CUs: wait until the stores have reached it, then count in
+    // Publish the partial at agent scope, wherever the tile's other chunks
+    // run: every wave waits until its stores have reached the L2, the
+    // barrier orders them before thread 0's counter update, whose release
+    // half writes the L2 back so that every XCD can see them; the acquire
+    // half of the last arriver's update invalidates its caches, and the
+    // second barrier orders every wave's partial loads after it.  (The
+    // dispatcher's placement keeps the chunks of a tile on one XCD, but the
+    // result does not rely on it.)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) arrival = __hip_atomic_fetch_add(S.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) arrival = __hip_atomic_fetch_add(S.cnt + t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrival != (unsigned)(S.s - 1)) return false;
     if (tid == 0) __hip_atomic_store(S.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call

@@ -238,12 +238,13 @@ int rz_kquant_gemv(int qtype, const void* blocks, uint32_t n, uint32_t k, const 
 /*
  * Batch-size routing between the two ways to multiply by a K-quant weight
  * (cublas_prefill/mod.rs page, cublas_gemm_threshold: the pages take the
- * GEMV route below a row threshold, 4 by default):
+ * GEMV route for fewer rows than a threshold, 4 by default):
  *   returns 1 when 1 <= m <= RZ_KGEMV_ROUTE_MAX_M (take rz_kquant_gemv),
  *   0 otherwise (take rz_fp8_quant_act + rz_fp8_gemm; m == 0 is a no-op on
  *   either route).
- * The bound is measured on MI355X, not the pages' 4: at N=4608, K=3584 (Q4_K)
- * the GEMV takes 6.0 / 6.5 / 8.1 / 9.5 us at m = 1 / 2 / 3 / 4 against
+ * The bound comes from a measurement on MI355X and agrees with the pages'
+ * 4, except that m = 4 itself takes the GEMV: at N=4608, K=3584 (Q4_K) the
+ * GEMV takes 6.0 / 6.5 / 8.1 / 9.5 us at m = 1 / 2 / 3 / 4 against
  * 11.7-12.1 us for activation quantisation plus FP8 GEMM, and the FP8 route
  * wins at m = 8.  Host only; no device needed.
  */

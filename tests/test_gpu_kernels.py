@@ -460,6 +460,42 @@ def test_gemm_edge_split_plans(rz, m, n, k, full):
     assert (host(ws[:4 * tiles]) == 0).all()  # arrival counters left at zero for the next call
 
 
+def test_gemm_split_on_two_streams(rz):
+    # split-K GEMMs issued alternately on two streams through the binding's
+    # default workspace: each stream gets its own zero-filled workspace, so
+    # their counters and partial sums never mix
+    shapes = [(512, 3584, 3584), (80, 200, 768)]  # 128x128 in 2 chunks; 64x32 in 3 chunks
+    cur = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for m, n, k in shapes:
+        assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) > 0
+        g = np.random.Generator(np.random.PCG64(m + 5 * n + k))
+        mp = fp8_path.pad_m(m)
+        cases = []
+        for si in range(2):
+            a8 = _codes(g, (mp, k))
+            a8[m:] = 0
+            w8 = _codes(g, (n, k))
+            sc = np.array([1.0, 0.017 + 0.001 * si, 0, 0], np.float32)
+            cases.append((a8, w8, sc, dev(a8), dev(w8), dev(sc)))
+        for st in streams:
+            st.wait_stream(cur)  # inputs uploaded on the current stream
+        outs = [[], []]
+        for rep in range(3):
+            for si, st in enumerate(streams):
+                _, _, _, A, Wd, S = cases[si]
+                with torch.cuda.stream(st):
+                    outs[si].append(rz.rz_fp8_gemm(A, Wd, m, S, 0.0081, stream=st))
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, m - 1], g.choice(m, min(m, 40), replace=False)]))
+        for si in range(2):
+            a8, w8, sc = cases[si][:3]
+            yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], np.float32(0.0081))
+            for y in outs[si]:
+                err = np.abs(y.cpu().numpy()[rows].astype(np.float64) - yr)
+                assert (err <= tol).all(), f"shape {(m, n, k)} stream {si}: {(err > tol).sum()} out of bound"
+
+
 @pytest.mark.parametrize("m,k,ns", [
     (2048, 1024, (18944, 18944)),    # gate/up widths: one launch of 1184 tiles (all whole)
     (4096, 512, (3584, 512, 512)),   # q/k/v widths at M=4096: 288 tiles, one round + half tiles

@@ -6,8 +6,10 @@ weight, or (the way bench.py runs the FFN step) every weight of the step
 packed by one rz_fp8_pack_weights call and the GEMMs on one activation run
 by one rz_fp8_gemm_group call.  Packed bytes, scales and
 activation codes are compared bit for bit with the oracle; GEMM outputs are
-compared element by element on every row for the small configurations and
-on sampled rows (the oracle computes those rows exactly) at full size.
+compared element by element on every row (configurations 1, 2, 3 and 5) or
+on sampled rows (the 4096-row layers of configuration 4; the oracle computes
+those rows exactly); all 196 weights of configuration 4 are checked against
+the oracle's recorded hashes.
 """
 import numpy as np
 import pytest
@@ -129,8 +131,9 @@ def _sample_rows(m, count=64, seed=0):
 
 
 def test_config3_ffn_full_size(rz):
+    # every output row of gate, up and down against the oracle's exact sums
     for grp in W.config_groups(3):
-        run_group(rz, grp, rows=_sample_rows(grp.m, seed=grp.act_seed))
+        run_group(rz, grp)
 
 
 @pytest.mark.parametrize("layer", [0, W.CFG4_LAYERS - 1])
@@ -141,8 +144,35 @@ def test_config4_layer(rz, layer):
 
 def test_config3_bench_step(rz):
     # the FFN step exactly as bench.py launches it: gate, up and down packed in
-    # one call (one launch set), gate and up in one grouped GEMM launch
-    run_step(rz, W.config_groups(3), rows=lambda grp: _sample_rows(grp.m, seed=grp.act_seed + 1))
+    # one call (one launch set), gate and up in one grouped GEMM launch; every
+    # output row checked
+    run_step(rz, W.config_groups(3))
+
+
+def test_config4_all_weights_pack_golden(rz, golden):
+    # all 196 weights of the 28-layer sweep packed by one rz_fp8_pack_weights
+    # call; the codes (SHA-256), absmax and scale of every one equal the
+    # oracle's, as tests/golden/make_cfg4_pack_golden.py recorded them
+    import hashlib
+    want = {(int(f[0]), f[1]): f for f in golden("cfg4_pack_sha256.txt")}
+    assert len(want) == 7 * W.CFG4_LAYERS
+    specs, blocks = [], []
+    for layer in range(W.CFG4_LAYERS):
+        for grp in W.config_groups(4, layer=layer):
+            for gm in grp.gemms:
+                specs.append((layer, gm))
+                blocks.append(dev(W.weight_blocks(gm.qtype, gm.w_seed, gm.n, gm.k)))
+    print(f"\n  packing {len(specs)} weights in one call", flush=True)
+    outs = rz.rz_fp8_pack_weights([(gm.qtype, b, gm.n, gm.k, None) for (_, gm), b in zip(specs, blocks)])
+    torch.cuda.synchronize()
+    del blocks
+    for (layer, gm), (w8, scale, amax) in zip(specs, outs):
+        f = want[(layer, gm.name)]
+        assert (int(f[2]), int(f[3]), int(f[4])) == (gm.qtype, gm.n, gm.k)
+        assert hashlib.sha256(w8.cpu().numpy().tobytes()).hexdigest() == f[5], (layer, gm.name)
+        assert f"{int(np.float32(amax).view(np.uint32)):08x}" == f[6], (layer, gm.name, amax)
+        assert f"{int(np.float32(scale).view(np.uint32)):08x}" == f[7], (layer, gm.name, scale)
+    print(f"  {len(specs)} weights: codes, absmax and scales equal the oracle's", flush=True)
 
 
 def test_config2_grouped(rz):

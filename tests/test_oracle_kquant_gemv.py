@@ -6,6 +6,8 @@ indicator inputs that pick one sub-block or scale group, exact linearity in
 x, one-hot inputs against the independently pinned dequant, and the fp32
 error bound against simulated fp32 accumulation in several orders.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -163,3 +165,30 @@ def test_rejects_bad_shapes():
         kquant_gemv.gemv(12, blocks, 1, 300, np.zeros((1, 300), np.float32))
     with pytest.raises(ValueError):
         kquant_gemv.gemv(12, blocks, 1, 256, np.zeros((1, 512), np.float32))
+
+
+def test_bound_equals_gamma_times_abs_sum_exactly():
+    # The bound is gamma_K * sum_k |x_k w_k| with gamma_K = K u / (1 - K u),
+    # u = 2^-24.  Here every weight is known in closed form (uniform quants:
+    # w = d*s*q_j - dmin*t per row, as in the closed-form test above), so the
+    # exact rational value is computed without the oracle's dequant and the
+    # float64 result must equal it up to float64 rounding: a bound that is
+    # too loose (or too tight) by any factor fails.
+    n, k = 4, 768
+    scales = bytes([3, 3, 3, 3, 2, 2, 2, 2, 3 | (2 << 4), 3 | (2 << 4), 3 | (2 << 4), 3 | (2 << 4)])
+    rows = [_q4k_blocks(k // 256, d=F16_HALF, dmin=F16_QUARTER, scales=scales, q=j) for j in range(n)]
+    blocks = np.concatenate(rows)
+    g = np.random.Generator(np.random.PCG64(41))
+    x = g.standard_normal((2, k)).astype(np.float32)
+    bd = kquant_gemv.bound(12, blocks, n, k, x)
+    u = Fraction(1, 2 ** 24)
+    gamma = k * u / (1 - k * u)
+    for i in range(2):
+        sx = sum(abs(Fraction(float(v))) for v in x[i])
+        for j in range(n):
+            wj = Fraction(1, 2) * 3 * j - Fraction(1, 4) * 2  # every weight of row j
+            exact = gamma * sx * abs(wj)
+            assert abs(Fraction(float(bd[i, j])) - exact) <= exact * Fraction(1, 2 ** 50), (i, j)
+    # row 0 has w = -1/2 everywhere: nonzero bound; a zero activation row gives 0
+    assert (bd > 0).all()
+    assert (kquant_gemv.bound(12, blocks, n, k, np.zeros((1, k), np.float32)) == 0).all()

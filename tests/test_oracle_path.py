@@ -151,3 +151,29 @@ def test_gemm_zero_rows_give_zero():
     w8 = np.random.Generator(np.random.PCG64(4)).integers(0, 0x7F, size=(3, 256)).astype(np.uint8)
     assert (fp8_path.gemm(a8, w8, 16, 2.0, 3.0) == 0).all()
     assert (fp8_path.bound(a8, w8, 16, 2.0, 3.0) == 0).all()
+
+
+def test_gemm_rows_selects_rows_of_full_gemm_and_bound():
+    # gemm_rows serves every sampled-row GPU check: it must equal the pinned
+    # full gemm/bound restricted to the requested rows, in the requested
+    # order, for unsorted and repeated rows and for the last real row m-1.
+    m, n, k = 37, 6, 512
+    g = np.random.Generator(np.random.PCG64(9))
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    a8 = np.zeros((fp8_path.pad_m(m), k), np.uint8)
+    a8[:m] = g.choice(codes, size=(m, k))
+    w8 = g.choice(codes, size=(n, k))
+    dqa, dqw = np.float32(0.011), np.float32(3.7e-4)
+    full = fp8_path.gemm(a8, w8, m, dqa, dqw)
+    tol_full = fp8_path.bound(a8, w8, m, dqa, dqw)
+    rows = [m - 1, 3, 3, 0, 17, m - 1, 20]
+    y, tol = fp8_path.gemm_rows(a8, w8, rows, dqa, dqw)
+    assert y.shape == (len(rows), n) and tol.shape == (len(rows), n)
+    np.testing.assert_array_equal(y, full[rows])
+    np.testing.assert_array_equal(tol, tol_full[rows])
+    # and a single row against brute force over Fractions (independent decoder)
+    A, Wd = _torch_decode(a8), _torch_decode(w8)
+    for j in range(n):
+        s = sum(Fraction(float(A[m - 1, t])) * Fraction(float(Wd[j, t])) for t in range(k))
+        exact = s * Fraction(float(dqa)) * Fraction(float(dqw))
+        assert abs(Fraction(float(y[0, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
