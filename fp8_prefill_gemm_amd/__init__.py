@@ -42,6 +42,7 @@ _SIGS = {
     "rz_fp8_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "rz_fp8_pack_weights": (_i32, [_u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "rz_fp8_quant_act": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp, _vp]),
+    "rz_fp8_quant_act_noalloc": (_i32, [_vp, _u32, _u32, _vp, _vp, _vp]),
     "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
     "rz_fp8_gemm_group": (_i32, [_vp, _u32, _u32, _vp, _u32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -215,6 +216,17 @@ def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
         ws = workspace(dev, stream)
     _check(lib().rz_fp8_quant_act(_ptr(x), m, k, _ptr(a_fp8), _ptr(act_scale), _ptr(ws),
                                   _stream(stream, dev)))
+    return a_fp8, act_scale
+
+
+def rz_fp8_quant_act_noalloc(x, a_fp8, act_scale, stream=None):
+    """rz_fp8_quant_act into caller-provided outputs, with the library's
+    per-GPU scratch array instead of a workspace: the call allocates
+    nothing (calls that overlap on one GPU race on that array)."""
+    _require_cuda(x, a_fp8, act_scale)
+    m, k = x.shape
+    _check(lib().rz_fp8_quant_act_noalloc(_ptr(x), m, k, _ptr(a_fp8), _ptr(act_scale),
+                                          _stream(stream, x.device)))
     return a_fp8, act_scale
 
 

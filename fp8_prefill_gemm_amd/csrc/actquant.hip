@@ -13,8 +13,17 @@
 // those keys in every workgroup, so no zeroing and no extra launch is
 // needed, and workgroup 0 publishes {absmax, absmax'/448} for the GEMM.
 // HBM traffic: read x twice (4 + 4 bytes per element) and write 1 byte.
+#include <mutex>
+
 #include "rz_device.h"
 #include "rz_internal.h"
+
+// Scratch of rz_fp8_quant_act_noalloc: the partial absmax keys of one
+// activation quantisation (at most kMaxPartials of them).  One copy per GPU,
+// held until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device
+// (quant_scratch_ptr), never through this name.
+static __device__ __align__(256) uint32_t scratch[rz::kMaxPartials];
 
 namespace rz {
 namespace {
@@ -157,6 +166,28 @@ hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_
     act_encode_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, partial, g1, a_fp8,
                                                act_scale);
     return hipGetLastError();
+}
+
+int quant_act_partials(uint64_t count_real) { return absmax_groups(count_real); }
+
+hipError_t quant_scratch_ptr(uint8_t** ptr) {
+    constexpr int kDevs = 64;
+    static std::mutex mu;
+    static void* addr[kDevs];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevs) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = static_cast<uint8_t*>(addr[dev]);
+    return hipSuccess;
 }
 
 hipError_t launch_absmax(const float* x, uint64_t count, float* out, uint8_t* ws, hipStream_t st) {

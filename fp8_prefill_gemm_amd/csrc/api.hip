@@ -345,6 +345,30 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, flo
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
+static_assert(rz::kQuantScratchBytes == RZ_QUANT_SCRATCH_BYTES, "scratch size in the header");
+
+int rz_fp8_quant_act_noalloc(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, float* act_scale_dev,
+                             void* stream) {
+    static const char* fn = "rz_fp8_quant_act_noalloc";
+    if ((m != 0 && (!x || !a_fp8)) || !act_scale_dev) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (int r = check_k(fn, k)) return r;
+    if ((uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || m > 0xFFFFFFF0u)
+        return fail(RZ_ERR_SHAPE, "%s: m*k too large", fn);
+    const uint64_t need = 4 * (uint64_t)rz::quant_act_partials((uint64_t)m * k);
+    if (need > RZ_QUANT_SCRATCH_BYTES)
+        return fail(RZ_ERR_SHAPE, "%s: %llu bytes of scratch needed, %u available", fn,
+                    (unsigned long long)need, (unsigned)RZ_QUANT_SCRATCH_BYTES);
+    if ((m != 0 && (!aligned16(x) || !aligned16(a_fp8))) || ((uintptr_t)act_scale_dev & 3u))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    uint8_t* scratch = nullptr;
+    hipError_t e = rz::quant_scratch_ptr(&scratch);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8, act_scale_dev, scratch,
+                             as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
 int rz_fp8_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n, uint32_t k,
                 const float* act_scale_dev, float w_scale, float* y, void* ws, size_t ws_bytes,
                 void* stream) {

@@ -67,6 +67,12 @@ hipError_t launch_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float*
 // ---- actquant.hip
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,
                             uint8_t* a_fp8, float* act_scale, uint8_t* ws, hipStream_t st);
+// Partial keys launch_quant_act writes for count_real elements (<= kMaxPartials).
+int quant_act_partials(uint64_t count_real);
+// Device address of the quantisation scratch array (kQuantScratchBytes) of
+// the current device, looked up once per device.
+constexpr size_t kQuantScratchBytes = 4 * (size_t)kMaxPartials;
+hipError_t quant_scratch_ptr(uint8_t** ptr);
 hipError_t launch_absmax(const float* x, uint64_t count, float* out, uint8_t* ws, hipStream_t st);
 hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* out,
                          hipStream_t st);

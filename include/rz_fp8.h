@@ -141,6 +141,31 @@ int rz_fp8_pack_weights(uint32_t count, const int* qtypes, const void* const* bl
 int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
                      float* act_scale_dev, void* ws, void* stream);
 
+/* Bytes of the device scratch array rz_fp8_quant_act_noalloc uses on each
+ * GPU (2048 partial absmax keys). */
+#define RZ_QUANT_SCRATCH_BYTES 8192u
+
+/*
+ * rz_fp8_quant_act without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and error behaviour as rz_fp8_quant_act, minus `ws`.
+ *
+ * Its scratch (the partial absmax keys) is a fixed array of
+ * RZ_QUANT_SCRATCH_BYTES in the library's device image, one copy per GPU,
+ * held until the process ends; its address is looked up on the first call
+ * on each device.  A quantisation needs at most 2048 keys whatever m*k
+ * (the reduction caps its grid), so every size accepted by rz_fp8_quant_act
+ * fits; a size that would need more is rejected with RZ_ERR_SHAPE.  Nothing
+ * in the scratch needs to start at zero: every call writes the keys it
+ * reads.  All calls on one GPU share the array, so calls that overlap in
+ * time on one GPU (different streams, or other host threads) race and must
+ * be ordered by the caller; calls on one stream are ordered by the stream.
+ * Calls no hipMalloc, hipFree or allocating library routine.
+ */
+int rz_fp8_quant_act_noalloc(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
+                             float* act_scale_dev, void* stream);
+
 /*
  * FP8 GEMM with fused dequantisation epilogue (gemm.rs page,
  * cublas_prefill_fp8_gemm steps 3-4; mod.rs page, F16_TO_F32_ACT_SCALED_PTX).
