@@ -34,6 +34,10 @@ shapes (warm, random E4M3 codes) and the 28-layer M=4096 sweep from them.
 --small-m instead times the small-batch routes (GEMV straight from K-quant
 blocks, FP8 GEMM, activation quantisation + FP8 GEMM) at N=4608, K=3584.
 
+--fp16-gemm instead times the FP16 cached-weight comparator (fp16 weight
+cache, fp16 activation, fp16 MFMA GEMM) beside the FP8 path on the FFN
+shapes at M=2048, with both paths' accuracy on the gate GEMM.
+
 --kquant-gemm instead times the FP8 GEMM that encodes the weight from its
 K-quant blocks inside the kernel (no FP8 weight cache) beside the cached
 path's GEMM, at the model's prefill shapes (warm).
@@ -429,6 +433,89 @@ def kquant_gemm(args, dev) -> int:
     return 0
 
 
+def fp16_gemm(args, dev) -> int:
+    """The FP16 comparator (cached fp16 weight, fp16 activation, fp16 MFMA
+    GEMM with fp32 accumulation) beside the FP8 path on the FFN shapes at
+    M=2048 (one line): warm GEMM times (HIP events around 20 launches after
+    5 warm-up launches), the one-off weight conversion and the per-input
+    activation conversion, the resident weight bytes, and the accuracy of
+    both paths' gate outputs on 64 rows against a float64 product of the
+    fp32 activation and the fp32 dequantised weight (computed here with
+    torch in float64 on the GPU from rz_dequant_f32)."""
+    import numpy as np
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    ffn, down = W.config_groups(3)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=20):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    rows, acc = {}, {}
+    for grp in (ffn, down):
+        x = torch.from_numpy(grp.activation()).to(dev)
+        m = grp.m
+        a16 = rz.rz_fp16_convert_act(x, stream=stream)
+        a8, sc = rz.rz_fp8_quant_act(x, stream=stream)
+        t_cvt16 = timed(lambda: rz.rz_fp16_convert_act(x, a16, stream))
+        t_q8 = timed(lambda: rz.rz_fp8_quant_act(x, a8, sc, stream=stream))
+        for gm in grp.gemms:
+            blocks = torch.from_numpy(W.weight_blocks(gm.qtype, gm.w_seed, gm.n, gm.k)).to(dev)
+            w16 = rz.rz_fp16_pack_weight(gm.qtype, blocks, gm.n, gm.k, stream=stream)
+            w8, scale, _ = rz.rz_fp8_pack_weight(gm.qtype, blocks, gm.n, gm.k, stream=stream)
+            t_pack16 = timed(lambda: rz.rz_fp16_pack_weight(gm.qtype, blocks, gm.n, gm.k, w16, stream), reps=5)
+            y16 = torch.empty((m, gm.n), dtype=torch.float32, device=dev)
+            y8 = torch.empty((m, gm.n), dtype=torch.float32, device=dev)
+            t16 = timed(lambda: rz.rz_fp16_gemm(a16, w16, m, y16, stream))
+            t8 = timed(lambda: rz.rz_fp8_gemm(a8, w8, m, sc, scale, y8, stream))
+            fl = 2.0 * m * gm.n * gm.k
+            rows[gm.name] = {"m": m, "n": gm.n, "k": gm.k,
+                             "fp16_gemm_us": round(t16 * 1e6, 1), "fp16_tflops": round(fl / t16 / 1e12, 1),
+                             "fp8_gemm_us": round(t8 * 1e6, 1), "fp8_tflops": round(fl / t8 / 1e12, 1),
+                             "fp16_weight_convert_us": round(t_pack16 * 1e6, 1),
+                             "act_convert_us": {"fp16": round(t_cvt16 * 1e6, 1), "fp8": round(t_q8 * 1e6, 1)},
+                             "weight_bytes": {"fp16": 2 * gm.n * gm.k, "fp8": gm.n * gm.k,
+                                              "kquant": int(blocks.numel())}}
+            log(f"{gm.name}: {rows[gm.name]}")
+            if gm.name == "gate":
+                wf = rz.rz_dequant_f32(gm.qtype, blocks, gm.n, gm.k, stream=stream)
+                sel = torch.linspace(0, m - 1, 64, device=dev).long()
+                ref = x[sel].double() @ wf.double().t()
+                den = ref.abs().mean().item()
+                for name, yy in (("fp16", y16), ("fp8", y8)):
+                    e = (yy[sel].double() - ref).abs()
+                    acc[name] = {"mean_abs_err_rel": round(e.mean().item() / den, 6),
+                                 "max_abs_err_rel": round(e.max().item() / den, 6)}
+                del wf, ref
+            del blocks, w16, w8, y16, y8
+        del x, a16, a8
+    g = rows["gate"]
+    ach = 2.0 * g["m"] * g["n"] * g["k"] / (g["fp16_gemm_us"] * 1e-6) / 1e12
+    plan = rz.rz_fp8_gemm_plan(g["m"], g["n"], 2 * g["k"])
+    roof = {"kernel": f"fp8_gemm_interior_kernel<fp16 operands>, {plan[0]}x{plan[1]} tiles, {plan[3]} workgroups "
+                      "(M=2048, N=18944, K=3584)",
+            "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(ach / 2500.0, 4), "traffic": None}
+    out = {"metric": "FP16 cached-weight GEMM vs FP8 GEMM, FFN at M=2048 (warm)", "unit": "us",
+           "higher_is_better": False, "rows": rows, "roofline": roof,
+           "gate_accuracy_vs_fp64_of_fp32_inputs": acc,
+           "dtype": "fp16 (fp32 accumulate) vs fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+           "config": {"workload": "FFN prefill, M=2048: gate/up K=3584 N=18944 Q4_K, down K=18944 N=3584 Q6_K"}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -445,6 +532,8 @@ def main() -> int:
                     help="instead time the FP8 GEMM alone at every configuration's shapes (warm)")
     ap.add_argument("--small-m", type=int, nargs="*", default=None,
                     help="instead time the small-batch paths at N=4608, K=3584 (Q4_K) for these m")
+    ap.add_argument("--fp16-gemm", action="store_true",
+                    help="instead time the FP16 cached-weight comparator beside the FP8 path (warm, M=2048 FFN)")
     ap.add_argument("--kquant-gemm", action="store_true",
                     help="instead time the GEMM straight from K-quant blocks beside the cached path (warm)")
     args = ap.parse_args()
@@ -481,6 +570,8 @@ def main() -> int:
         return gemm_shapes(args, dev)
     if args.kquant_gemm:
         return kquant_gemm(args, dev)
+    if args.fp16_gemm:
+        return fp16_gemm(args, dev)
     if args.small_m is not None:
         if not args.small_m:
             args.small_m = [1, 2, 3, 4, 8, 37]

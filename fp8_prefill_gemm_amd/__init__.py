@@ -46,6 +46,9 @@ _SIGS = {
     "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
     "rz_fp8_gemm_group": (_i32, [_vp, _u32, _u32, _vp, _u32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "rz_fp16_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
+    "rz_fp16_convert_act": (_i32, [_vp, _u32, _u32, _vp, _vp]),
+    "rz_fp16_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _vp]),
     "rz_dequant_f32": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
     "rz_absmax_f32": (_i32, [_vp, _u64, _vp, _vp, _vp]),
     "rz_e4m3_encode": (_i32, [_vp, _u64, _f32, _vp, _vp]),
@@ -350,6 +353,39 @@ def rz_fp8_gemm_group(a_fp8, m: int, act_scale, weights, ys=None, stream=None, w
                                    ctypes.addressof(nn), ctypes.addressof(sc), ctypes.addressof(yp), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream, dev)))
     return ys
+
+
+def rz_fp16_pack_weight(qtype: int, blocks, n: int, k: int, w_f16=None, stream=None):
+    """-> fp16 [n][k]: the dequantised weight rounded to fp16 (the FP16
+    comparator's weight cache)."""
+    torch = _torch()
+    _require_cuda(blocks, w_f16)
+    if w_f16 is None:
+        w_f16 = _empty((n, k), torch.float16, blocks.device, stream)
+    _check(lib().rz_fp16_pack_weight(qtype, _ptr(blocks), n, k, _ptr(w_f16), _stream(stream, blocks.device)))
+    return w_f16
+
+
+def rz_fp16_convert_act(x, a_f16=None, stream=None):
+    """x fp32 [m][k] -> fp16 [pad_m(m)][k] (pad rows zero)."""
+    torch = _torch()
+    _require_cuda(x, a_f16)
+    m, k = x.shape
+    if a_f16 is None:
+        a_f16 = _empty((rz_pad_m(m), k), torch.float16, x.device, stream)
+    _check(lib().rz_fp16_convert_act(_ptr(x), m, k, _ptr(a_f16), _stream(stream, x.device)))
+    return a_f16
+
+
+def rz_fp16_gemm(a_f16, w_f16, m: int, y=None, stream=None):
+    """-> y fp32 [m][n] = a_f16[:m] @ w_f16^T (fp32 accumulation, no scales)."""
+    torch = _torch()
+    _require_cuda(a_f16, w_f16, y)
+    n, k = w_f16.shape
+    if y is None:
+        y = _empty((m, n), torch.float32, w_f16.device, stream)
+    _check(lib().rz_fp16_gemm(_ptr(a_f16), _ptr(w_f16), m, n, k, _ptr(y), _stream(stream, w_f16.device)))
+    return y
 
 
 def rz_dequant_f32(qtype: int, blocks, n: int, k: int, out=None, stream=None):

@@ -102,6 +102,31 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(
     }
 }
 
+// fp32 -> fp16 (to nearest even) of the activation for the FP16 comparator
+// path (gemm.rs page, cublas_prefill_hgemm; mod.rs page, F32_TO_F16_PTX):
+// 8 elements per thread and iteration; groups at or past count_real (a
+// multiple of 256) are the pad rows and are written as zeros.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, (h2v){(_Float16)a, (_Float16)b});
+}
+
+__global__ __launch_bounds__(kThreads) void act_to_f16_kernel(const float* __restrict__ x, uint64_t count_real,
+                                                              uint64_t count_total, uint16_t* __restrict__ out) {
+    const uint64_t groups = count_total >> 3, real_groups = count_real >> 3;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    uint4* o = reinterpret_cast<uint4*>(out);
+    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += stride) {
+        if (g < real_groups) {
+            const float4 a = x4[2 * g], b = x4[2 * g + 1];
+            o[g] = make_uint4(f16x2(a.x, a.y), f16x2(a.z, a.w), f16x2(b.x, b.y), f16x2(b.z, b.w));
+        } else {
+            o[g] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
 // Final reduction for the absmax diagnostic: one workgroup.
 __global__ __launch_bounds__(kThreads) void absmax_final_kernel(const uint32_t* __restrict__ partial,
                                                                 int npartial, float* __restrict__ out) {
@@ -188,6 +213,12 @@ hipError_t quant_scratch_ptr(uint8_t** ptr) {
     }
     *ptr = static_cast<uint8_t*>(addr[dev]);
     return hipSuccess;
+}
+
+hipError_t launch_fp16_convert(const float* x, uint64_t count_real, uint64_t count_total, uint16_t* out,
+                               hipStream_t st) {
+    act_to_f16_kernel<<<grid_for(count_total >> 3, 8192), kThreads, 0, st>>>(x, count_real, count_total, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_absmax(const float* x, uint64_t count, float* out, uint8_t* ws, hipStream_t st) {

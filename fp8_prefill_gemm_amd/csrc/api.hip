@@ -436,7 +436,7 @@ int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float*
                 G.w_scale[G.count] = w_scale[i];
                 ++G.count;
             }
-            const hipError_t e = rz::launch_interior(p, a_fp8, G, m, (uint32_t)ntot, k, act_scale_dev, st);
+            const hipError_t e = rz::launch_interior(p, a_fp8, G, m, (uint32_t)ntot, k, act_scale_dev, st, false);
             return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
         }
     }
@@ -447,6 +447,51 @@ int rz_fp8_gemm_group(const uint8_t* a_fp8, uint32_t m, uint32_t k, const float*
         if (e != hipSuccess) return hip_fail(e, fn);
     }
     return RZ_OK;
+}
+
+int rz_fp16_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint16_t* w_f16, void* stream) {
+    static const char* fn = "rz_fp16_pack_weight";
+    if (!blocks || !w_f16) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if (!qtype_ok(qtype)) return fail(RZ_ERR_QTYPE, "%s: unsupported qtype %d", fn, qtype);
+    if (int r = check_k(fn, k)) return r;
+    if (n == 0) return fail(RZ_ERR_SHAPE, "%s: n must be positive", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: n*k too large", fn);
+    if (!aligned16(blocks) || !aligned16(w_f16))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_fp16_pack(qtype, static_cast<const uint8_t*>(blocks), (uint64_t)n * (k / 256u), w_f16,
+                                        as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_fp16_convert_act(const float* x, uint32_t m, uint32_t k, uint16_t* a_f16, void* stream) {
+    static const char* fn = "rz_fp16_convert_act";
+    if (int r = check_k(fn, k)) return r;
+    if (m == 0) return RZ_OK;  // nothing to read or write
+    if (!x || !a_f16) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || m > 0xFFFFFFF0u) return fail(RZ_ERR_SHAPE, "%s: m*k too large", fn);
+    if (!aligned16(x) || !aligned16(a_f16))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_fp16_convert(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_f16, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32_t m, uint32_t n, uint32_t k, float* y,
+                 void* stream) {
+    static const char* fn = "rz_fp16_gemm";
+    if (int r = check_k(fn, k)) return r;
+    if (k > RZ_MAX_GEMM_K / 2) return fail(RZ_ERR_SHAPE, "%s: k=%u exceeds %u", fn, k, (unsigned)(RZ_MAX_GEMM_K / 2));
+    if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
+    if (!a_f16 || !w_f16 || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)n * k > RZ_MAX_ELEMS || (uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || (uint64_t)m * n > RZ_MAX_ELEMS ||
+        m > 0x7FFFFFF0u || n > 0x7FFFFFF0u)
+        return fail(RZ_ERR_SHAPE, "%s: operand too large", fn);
+    if (!aligned16(a_f16) || !aligned16(w_f16) || !aligned16(y))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_fp16_gemm(a_f16, w_f16, m, n, k, y, device_cus(), as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
 int rz_route_kquant_gemv(uint32_t m) { return m >= 1u && m <= RZ_KGEMV_ROUTE_MAX_M ? 1 : 0; }

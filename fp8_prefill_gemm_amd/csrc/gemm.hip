@@ -92,7 +92,7 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* base, uint32_t lo, uint32_
 // TM = 4, 3 for TM = 2).  A chunk load therefore has two full steps to land
 // before the same group of the step after next writes it to LDS.  The
 // caller places a workgroup barrier after each step.
-template <int TM>
+template <int TM, bool F16>
 __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, uint8_t* nxt,
                                       u32x4 (&x)[8 + 2 * TM], __amdgpu_buffer_rsrc_t wrs,
                                       __amdgpu_buffer_rsrc_t ars, uint32_t voff, uint32_t kb, uint32_t step,
@@ -102,6 +102,7 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
     constexpr int kGroups = 2 * TM;
     constexpr int kPer = (8 + 2 * TM) / kGroups;  // chunks per group
     constexpr int kA1 = TM == 4 ? 1 : 0;          // groups kA1, kA1+1 read the second K half's weights
+    constexpr int kMf = F16 ? 2 : 1;              // MFMA instructions per mma32
     v8i a[2][4];
     v8i b[2];
     // b first: LDS reads complete in order, so MFMA i of group 0 waits only
@@ -123,8 +124,7 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[g & 1], a[kk][i], acc[i][j], 0, 0, 0,
-                                                                        0, 0, 0);
+            acc[i][j] = mma32<F16>(b[g & 1], a[kk][i], acc[i][j]);
 #pragma unroll
         for (int c = kPer * g; c < kPer * g + kPer; ++c) {
             *reinterpret_cast<u32x4*>(nxt + (c >> 3) * 256 * kBK + (c & 7) * kRow32 + o.st) = x[c];
@@ -141,13 +141,13 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
             else if (g < 7)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
         } else {
             if (g == 0)
@@ -158,11 +158,11 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -194,7 +194,7 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
 // K-step t computes from LDS slot t%2 while register set (t%2 ? xq : xp)
 // moves the data of step t+1 into the other slot and is refilled with step
 // t+3; so each load has two steps of MFMA work to land.
-template <int TM>
+template <int TM, bool F16>
 __device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][TM], uint8_t (&smem)[2][512 * kBK],
                                               __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t ars,
                                               uint32_t voff, uint32_t step, int KS, const PipeOffsets& po) {
@@ -225,12 +225,12 @@ __device__ __forceinline__ void tile_mainloop(v16f (&acc)[4][TM], uint8_t (&smem
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < KS; kt += 2) {
         const bool in3 = kt + 3 < KS, in4 = kt + 4 < KS;
-        kstep<TM>(acc, smem[0], smem[1], xp, in3 ? wrs : zr, in3 ? ars : zr, voff, (uint32_t)(kt + 3) * kBK, step,
-                  po);
+        kstep<TM, F16>(acc, smem[0], smem[1], xp, in3 ? wrs : zr, in3 ? ars : zr, voff, (uint32_t)(kt + 3) * kBK,
+                       step, po);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        kstep<TM>(acc, smem[1], smem[0], xq, in4 ? wrs : zr, in4 ? ars : zr, voff, (uint32_t)(kt + 4) * kBK, step,
-                  po);
+        kstep<TM, F16>(acc, smem[1], smem[0], xq, in4 ? wrs : zr, in4 ? ars : zr, voff, (uint32_t)(kt + 4) * kBK,
+                       step, po);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -312,6 +312,9 @@ __device__ __forceinline__ int group_of(const GemmGroups& G, int& n0, int& N) {
     return g;
 }
 
+// F16: fp16 operands (K is then the row length in bytes, twice the
+// element count), no scales (act_scale is not read, w_scale is 1).
+template <bool F16>
 __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* __restrict__ A, GemmGroups G,
                                                                 int M, int N, int K,
                                                                 const float* __restrict__ act_scale,
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     const int wn = wid & 1, wm = wid >> 1;
     const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
     const uint32_t step = 32u * (uint32_t)K;
-    const float act_dq = act_scale[1];
+    const float act_dq = F16 ? 1.0f : act_scale[1];
     const int mp = (M + 15) & ~15;  // >= 256 here
     int t, n0, m0;
     if (bid < P.nwhole) {
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
         const int g = group_of(G, n0, Ng);
         const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
         v16f acc[4][4];
-        tile_mainloop<4>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
+        tile_mainloop<4, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
                          tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
         store_acc<4>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
                      act_dq * G.w_scale[g]);
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     const int g = group_of(G, n0, Ng);
     const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
     v16f acc[4][2];
-    tile_mainloop<2>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
+    tile_mainloop<2, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
                      tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
     store_acc<2>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
                  act_dq * G.w_scale[g]);
@@ -469,11 +472,39 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
     G.w[0] = w_fp8;
     G.y[0] = y;
     G.w_scale[0] = w_scale;
-    return launch_interior(p, a_fp8, G, m, n, k, act_scale, st);
+    return launch_interior(p, a_fp8, G, m, n, k, act_scale, st, false);
+}
+
+hipError_t launch_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32_t m, uint32_t n, uint32_t k,
+                            float* y, int cus, hipStream_t st) {
+    const uint32_t kb = 2u * k;  // row length in bytes: the kernels walk K in 128-byte steps
+    GemmPlan p = plan_gemm(m, n, kb, cus, false);
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(a_f16);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(w_f16);
+    if (p.kind != kGemmTiles) {
+        // no GEMV or skinny kernel for fp16 operands: small M takes the 64x32 tiles
+        if (p.kind == kGemmGemv || p.kind == kGemmSkinny) {
+            p.kind = kGemmSmall;
+            p.bn = kKinds[kGemmSmall].bn;
+            p.bm = kKinds[kGemmSmall].bm;
+            p.threads = kKinds[kGemmSmall].threads;
+            const int mp = (int)((m + 15u) & ~15u);
+            p.workgroups = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
+            p.s = 1;
+        }
+        return launch_gemm_edge_fp16(p, a, w, m, n, kb, y, st);
+    }
+    GemmGroups G = {};
+    G.count = 1;
+    G.n_end[0] = (int)n;
+    G.w[0] = w;
+    G.y[0] = y;
+    G.w_scale[0] = 1.0f;
+    return launch_interior(p, a, G, m, n, kb, nullptr, st, true);
 }
 
 hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGroups& G, uint32_t m, uint32_t n,
-                           uint32_t k, const float* act_scale, hipStream_t st) {
+                           uint32_t k, const float* act_scale, hipStream_t st, bool f16) {
     const int mp = (int)((m + 15u) & ~15u);
     const int tiles_m = ceil_div(mp, 256);
     InteriorPlan ip;
@@ -490,8 +521,12 @@ hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGr
     int hgm = 1;
     while (hgm * 2 <= ip.halves_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
     ip.half_gm = hgm;
-    fp8_gemm_interior_kernel<<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n, (int)k,
-                                                                             act_scale, ip);
+    if (f16)
+        fp8_gemm_interior_kernel<true><<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n,
+                                                                                      (int)k, act_scale, ip);
+    else
+        fp8_gemm_interior_kernel<false><<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n,
+                                                                                       (int)k, act_scale, ip);
     return hipGetLastError();
 }
 

@@ -12,6 +12,30 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // class whose copies become memcpy and keep the staging arrays in memory).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// One 32x32 output block times one 32-byte K fragment per lane (src0: the
+// rows of the result, src1: its columns; lane l holds row / column l % 32).
+//   FP8 (E4M3 codes): one v_mfma_f32_32x32x64_f8f6f4, 64 K values;
+//   F16: the fragment is 16 halves, so two v_mfma_f32_32x32x16_f16, on
+//        bytes 0..15 and 16..31 of every lane's fragment.  Inside each MFMA
+//        lanes 0-31 and 32-63 carry different K values; both operands come
+//        from the same LDS chunks in the same lane order, so every K value
+//        still meets its partner exactly once.
+template <bool F16>
+__device__ __forceinline__ v16f mma32(const v8i& src0, const v8i& src1, v16f acc) {
+    if constexpr (F16) {
+        const v8h a0 = __builtin_bit_cast(v8h, __builtin_shufflevector(src0, src0, 0, 1, 2, 3));
+        const v8h a1 = __builtin_bit_cast(v8h, __builtin_shufflevector(src0, src0, 4, 5, 6, 7));
+        const v8h b0 = __builtin_bit_cast(v8h, __builtin_shufflevector(src1, src1, 0, 1, 2, 3));
+        const v8h b1 = __builtin_bit_cast(v8h, __builtin_shufflevector(src1, src1, 4, 5, 6, 7));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(src0, src1, acc, 0, 0, 0, 0, 0, 0);
+    }
+}
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;

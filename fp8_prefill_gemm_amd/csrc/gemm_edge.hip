@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_clamped(u32x4 (&r)[L], const uint8_t* __res
 // All MFMAs of one 128-byte K-step for one wave: for each 64-byte half, the
 // wave's TN weight fragments stay in registers while its TM activation
 // fragments are read one at a time.
-template <int BN, int WTN, int WTM, int TN, int TM>
+template <int BN, int WTN, int WTM, int TN, int TM, bool F16>
 __device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* stage, int wn, int wm,
                                           int lane) {
     const uint8_t* sw = stage;
@@ -68,9 +68,7 @@ __device__ __forceinline__ void mma_stage(v16f (&acc)[TN][TM], const uint8_t* st
         for (int j = 0; j < TM; ++j) {
             const v8i bf = frag(sa, wm * WTM + j * 32 + (lane & 31), c0);
 #pragma unroll
-            for (int i = 0; i < TN; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af[i], acc[i][j], 0, 0,
-                                                                            0, 0, 0, 0);
+            for (int i = 0; i < TN; ++i) acc[i][j] = mma32<F16>(bf, af[i], acc[i][j]);
         }
     }
 }
@@ -170,7 +168,8 @@ __device__ __forceinline__ bool split_reduce(v16f (&acc)[TN][TM], const SplitK& 
     return true;
 }
 
-template <int BN, int BM, int WN, int WM, bool kSplit>
+// F16: fp16 operands (K = row bytes), no scales (act_scale not read).
+template <int BN, int BM, int WN, int WM, bool kSplit, bool F16 = false>
 __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
     int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
@@ -231,12 +230,12 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
         if (kt + 2 < KT) RZ_STAGE_LOAD(rw0, ra0, (k0 + kt + 2) * kBK);
-        mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[0], wn, wm, lane);
+        mma_stage<BN, WTN, WTM, TN, TM, F16>(acc, smem[0], wn, wm, lane);
         store_rows<LW, NT>(smem[1], rw1, tid);
         store_rows<LA, NT>(smem[1] + BN * kBK, ra1, tid);
         __syncthreads();
         if (kt + 3 < KT) RZ_STAGE_LOAD(rw1, ra1, (k0 + kt + 3) * kBK);
-        mma_stage<BN, WTN, WTM, TN, TM>(acc, smem[1], wn, wm, lane);
+        mma_stage<BN, WTN, WTM, TN, TM, F16>(acc, smem[1], wn, wm, lane);
         if (kt + 2 < KT) {
             store_rows<LW, NT>(smem[0], rw0, tid);
             store_rows<LA, NT>(smem[0] + BN * kBK, ra0, tid);
@@ -247,10 +246,11 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_deep_kernel(
 
     if constexpr (kSplit)  // (the 256x256 instance never splits: its registers are full)
         if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane, act_scale[1] * w_scale);
+    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                 F16 ? 1.0f : act_scale[1] * w_scale);
 }
 
-template <int BN, int BM, int WN, int WM>
+template <int BN, int BM, int WN, int WM, bool F16 = false>
 __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Wt, float* __restrict__ Y, int M,
     int Mp, int N, int K, const float* __restrict__ act_scale, float w_scale, int tiles_m,
@@ -313,9 +313,7 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
 #pragma unroll
             for (int i = 0; i < TN; ++i)
 #pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+                for (int j = 0; j < TM; ++j) acc[i][j] = mma32<F16>(bf[j], af[i], acc[i][j]);
         }
         if (more) {
             store_rows<LW, NT>(smem[(kt + 1) & 1], rw, tid);
@@ -326,7 +324,8 @@ __global__ __launch_bounds__(64 * WN * WM) void fp8_gemm_kernel(
 
     // ---- epilogue: y = acc * (s_act * s_w), fp32 row-major
     if (S.s > 1 && !split_reduce<TN, TM, NT>(acc, S, t, chunk, arrival, tid)) return;
-    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane, act_scale[1] * w_scale);
+    store_tile<TN, TM, WTN, WTM>(acc, Y, M, N, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                 F16 ? 1.0f : act_scale[1] * w_scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,6 +601,31 @@ hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8
             fp8_gemm_kernel<64, 32, 2, 1><<<p.workgroups, p.threads, 0, st>>>(
                 a_fp8, w_fp8, y, (int)m, mp, (int)n, (int)k, act_scale, w_scale, tiles_m, tiles_n, group_m, S);
             break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_edge_fp16(const GemmPlan& p, const uint8_t* a, const uint8_t* w, uint32_t m, uint32_t n,
+                                 uint32_t kb, float* y, hipStream_t st) {
+    const int mp = (int)((m + 15u) & ~15u);
+    const int tiles_m = (mp + p.bm - 1) / p.bm, tiles_n = ((int)n + p.bn - 1) / p.bn;
+    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    const SplitK S = {1, (int)(kb / 256u), nullptr, nullptr};
+    switch (p.kind) {
+        case kGemmLargeEdge:
+            fp8_gemm_deep_kernel<256, 256, 2, 2, false, true><<<p.workgroups, p.threads, 0, st>>>(
+                a, w, y, (int)m, mp, (int)n, (int)kb, nullptr, 1.0f, tiles_m, tiles_n, group_m, S);
+            break;
+        case kGemmMedium:
+            fp8_gemm_deep_kernel<128, 128, 2, 2, false, true><<<p.workgroups, p.threads, 0, st>>>(
+                a, w, y, (int)m, mp, (int)n, (int)kb, nullptr, 1.0f, tiles_m, tiles_n, group_m, S);
+            break;
+        case kGemmSmall:
+            fp8_gemm_kernel<64, 32, 2, 1, true><<<p.workgroups, p.threads, 0, st>>>(
+                a, w, y, (int)m, mp, (int)n, (int)kb, nullptr, 1.0f, tiles_m, tiles_n, group_m, S);
+            break;
+        default:
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

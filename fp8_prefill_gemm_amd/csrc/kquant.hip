@@ -117,6 +117,31 @@ __global__ __launch_bounds__(kThreads) void dequant_f32_kernel(const uint8_t* __
     });
 }
 
+// The fp16 weight cache of the FP16 comparator path (gemm.rs page,
+// get_or_cache_fp16_weight): every weight dequantised as above, then
+// rounded to fp16 (to nearest even, as cvt.rn.f16.f32 on the mod.rs page);
+// fp16 [N][K] row-major, 32 bytes per run of 16.
+// The pages round twice (the fp32 scratch value, then the fp16 conversion).
+// The empty asm makes the fp32 values exist as such: otherwise the compiler
+// folds the decode's fused multiply-add and the conversion into one
+// v_fma_mix*_f16, which rounds the exact value straight to fp16 and differs
+// from the two roundings at fp16 ties of the fp32 value.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2(float a, float b) {
+    asm("" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(uint32_t, (h2v){(_Float16)a, (_Float16)b});
+}
+
+template <int QT>
+__global__ __launch_bounds__(kThreads) void fp16_pack_kernel(const uint8_t* __restrict__ blocks, uint64_t nb,
+                                                             uint16_t* __restrict__ out) {
+    visit_runs<QT>(blocks, nb, [&](uint64_t base, const float* v) {
+        uint4* o = reinterpret_cast<uint4*>(out + base);
+        o[0] = make_uint4(f16x2(v[0], v[1]), f16x2(v[2], v[3]), f16x2(v[4], v[5]), f16x2(v[6], v[7]));
+        o[1] = make_uint4(f16x2(v[8], v[9]), f16x2(v[10], v[11]), f16x2(v[12], v[13]), f16x2(v[14], v[15]));
+    });
+}
+
 // Pass 1 of one weight: this workgroup's absmax key (from each unit's
 // extreme quants), reduced over the workgroup.
 template <int QT>
@@ -265,6 +290,15 @@ hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nb, flo
         dequant_f32_kernel<12><<<grid, kThreads, 0, st>>>(blocks, nb, out);
     else
         dequant_f32_kernel<14><<<grid, kThreads, 0, st>>>(blocks, nb, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp16_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint16_t* out, hipStream_t st) {
+    const int grid = clamp_groups(groups_for(qtype, nb, 2), 1 << 16);
+    if (qtype == 12)
+        fp16_pack_kernel<12><<<grid, kThreads, 0, st>>>(blocks, nb, out);
+    else
+        fp16_pack_kernel<14><<<grid, kThreads, 0, st>>>(blocks, nb, out);
     return hipGetLastError();
 }
 

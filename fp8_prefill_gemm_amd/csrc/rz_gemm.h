@@ -34,8 +34,10 @@ struct GemmGroups {
 };
 // The interior-tile kernel (p.kind == kGemmTiles, p planned for the total
 // width n = G.n_end[G.count - 1]).
+// f16: the operands are fp16 (k is then the row length in bytes) and there
+// are no scales (act_scale unused, every w_scale 1).
 hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGroups& G, uint32_t m, uint32_t n,
-                           uint32_t k, const float* act_scale, hipStream_t st);
+                           uint32_t k, const float* act_scale, hipStream_t st, bool f16);
 hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                        uint32_t k, const float* act_scale, float w_scale, float* y, void* ws,
                        size_t ws_bytes, int cus, hipStream_t st);
@@ -43,6 +45,14 @@ hipError_t launch_gemm(const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, u
 // the split-K counters and partial sums when p.s > 1.
 hipError_t launch_gemm_edge(const GemmPlan& p, const uint8_t* a_fp8, const uint8_t* w_fp8, uint32_t m, uint32_t n,
                             uint32_t k, const float* act_scale, float w_scale, float* y, void* ws, hipStream_t st);
+// y[m][n] = a[m][k] * w[n][k]^T over fp16 operands (a: pad16(m) rows), fp32
+// accumulation and output, no scales; k in elements.  Never splits K.
+hipError_t launch_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32_t m, uint32_t n, uint32_t k,
+                            float* y, int cus, hipStream_t st);
+// The edge-capable plans of launch_gemm_edge on fp16 operands (kb = row
+// bytes; kinds kGemmLargeEdge, kGemmMedium, kGemmSmall; no split).
+hipError_t launch_gemm_edge_fp16(const GemmPlan& p, const uint8_t* a, const uint8_t* w, uint32_t m, uint32_t n,
+                                 uint32_t kb, float* y, hipStream_t st);
 // Split-K workspace: arrival counters of the split tiles (one uint32 each),
 // padded to 256 bytes; the partial sums follow.
 inline size_t split_counter_bytes(int tiles) { return ((size_t)tiles * sizeof(unsigned) + 255) / 256 * 256; }

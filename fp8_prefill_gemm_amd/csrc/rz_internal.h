@@ -57,6 +57,10 @@ hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* bl
                            uint8_t* const* w_fp8, uint8_t* ws, float* const* host_scale, const uint32_t* ticket,
                            hipStream_t st);
 
+// FP16 comparator: the K-quant weight dequantised and rounded to fp16
+// [nb*256] (row-major [N][K]).
+hipError_t launch_fp16_pack(int qtype, const uint8_t* blocks, uint64_t nb, uint16_t* out, hipStream_t st);
+
 // ---- kqgemm.hip
 // Y[m][n] = dec(A) * dec(E4M3(RN(w * w_q)))^T * (act_scale[1] * w_dq), the
 // weight codes made from the K-quant blocks inside the GEMM.
@@ -73,6 +77,9 @@ int quant_act_partials(uint64_t count_real);
 // the current device, looked up once per device.
 constexpr size_t kQuantScratchBytes = 4 * (size_t)kMaxPartials;
 hipError_t quant_scratch_ptr(uint8_t** ptr);
+// fp16 copy of x (count_real values, then zeros up to count_total).
+hipError_t launch_fp16_convert(const float* x, uint64_t count_real, uint64_t count_total, uint16_t* out,
+                               hipStream_t st);
 hipError_t launch_absmax(const float* x, uint64_t count, float* out, uint8_t* ws, hipStream_t st);
 hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* out,
                          hipStream_t st);

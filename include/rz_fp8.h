@@ -318,6 +318,44 @@ int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_
                        void* stream);
 
 /* ---------------------------------------------------------------------
+ * FP16 comparator: the cached-fp16-weight GEMM the FP8 path replaced
+ * (gemm.rs page, get_or_cache_fp16_weight and cublas_prefill_hgemm; mod.rs
+ * page, F32_TO_F16_PTX and the module note on the tensor-core speed-up).
+ * Kept to measure the FP8 path's speed and accuracy against it.
+ * --------------------------------------------------------------------- */
+
+/*
+ * The fp16 weight cache: w_f16[j][kk] = fp16(w[j][kk]) with w the weight
+ * decoded exactly as rz_dequant_f32 decodes it and fp16() the
+ * round-to-nearest-even conversion (|w| >= 65520 gives +-Inf).
+ *   blocks  device, n*(k/256) super-blocks, row-major (as rz_fp8_pack_weight)
+ *   w_f16   device out, fp16 bit patterns [n][k] row-major (2 bytes each)
+ * No workspace, no host synchronisation.
+ */
+int rz_fp16_pack_weight(int qtype, const void* blocks, uint32_t n, uint32_t k, uint16_t* w_f16,
+                        void* stream);
+
+/*
+ * The fp16 activation: a_f16[i][kk] = fp16(x[i][kk]) (round to nearest even)
+ * for i < m; rows m..rz_pad_m(m)-1 are zero.
+ *   x       device, fp32 [m][k] row-major
+ *   a_f16   device out, fp16 [rz_pad_m(m)][k] row-major
+ * m == 0 is a no-op (x and a_f16 may then be NULL).
+ */
+int rz_fp16_convert_act(const float* x, uint32_t m, uint32_t k, uint16_t* a_f16, void* stream);
+
+/*
+ * y[i][j] = sum_kk a_f16[i][kk] * w_f16[j][kk] for i < m, j < n: fp16
+ * operands, products exact, accumulated in fp32 on the matrix cores, fp32
+ * output [m][n] row-major; no scale factors.
+ *   a_f16   device, fp16 [rz_pad_m(m)][k] from rz_fp16_convert_act
+ *   w_f16   device, fp16 [n][k] from rz_fp16_pack_weight
+ * k <= RZ_MAX_GEMM_K / 2.  m == 0 or n == 0 is a no-op.  No workspace.
+ */
+int rz_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32_t m, uint32_t n, uint32_t k,
+                 float* y, void* stream);
+
+/* ---------------------------------------------------------------------
  * Diagnostics: the individual steps, exposed so that each can be checked
  * against the oracle.  Same conventions as above.
  * --------------------------------------------------------------------- */
