@@ -86,6 +86,20 @@ def dequant_q4k_blocks(blocks: np.ndarray) -> np.ndarray:
     return val.astype(np.float32)
 
 
+def q4k_parts(blocks: np.ndarray):
+    """The fields of Q4_K blocks [nb, 144] as exact numbers: (d, dmin)
+    float64 [nb], (sc, mn) int64 [nb, 8] per sub-block, q int64 [nb, 256];
+    element i of a block is d*sc[i//32]*q[i] - dmin*mn[i//32]."""
+    blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, Q4_K_BYTES)
+    sc, mn = q4k_scale_min(blocks[:, 4:16])
+    return _f16_at(blocks, 0), _f16_at(blocks, 2), sc, mn, q4k_quants(blocks[:, 16:144])
+
+
+def q4k_subblock_of() -> np.ndarray:
+    """Sub-block index (0..7) of each of the 256 elements of a super-block."""
+    return np.arange(QK_K) // 32
+
+
 def q6k_quants_scales(blocks: np.ndarray):
     """(q in 0..63, sub-block scale) int64 arrays [nb, 256] in element order."""
     ql = blocks[:, 0:128].astype(np.int64)
