@@ -46,6 +46,9 @@ _SIGS = {
     "rz_fp8_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _f32, _vp, _vp, ctypes.c_size_t, _vp]),
     "rz_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_u32, _u32, _u32]),
     "rz_fp8_gemm_group": (_i32, [_vp, _u32, _u32, _vp, _u32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "rz_q8_1_bytes": (ctypes.c_size_t, [_u32, _u32]),
+    "rz_q8_1_quant": (_i32, [_vp, _u32, _u32, _vp, _vp]),
+    "rz_q8_q4k_gemm": (_i32, [_vp, _u32, _vp, _u32, _u32, _vp, _vp]),
     "rz_fp16_pack_weight": (_i32, [_i32, _vp, _u32, _u32, _vp, _vp]),
     "rz_fp16_convert_act": (_i32, [_vp, _u32, _u32, _vp, _vp]),
     "rz_fp16_gemm": (_i32, [_vp, _vp, _u32, _u32, _u32, _vp, _vp]),
@@ -353,6 +356,27 @@ def rz_fp8_gemm_group(a_fp8, m: int, act_scale, weights, ys=None, stream=None, w
                                    ctypes.addressof(nn), ctypes.addressof(sc), ctypes.addressof(yp), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream, dev)))
     return ys
+
+
+def rz_q8_1_quant(x, q8=None, stream=None):
+    """x fp32 [m][k] -> Q8_1 blocks, uint8 [m][k/32][36]."""
+    torch = _torch()
+    _require_cuda(x, q8)
+    m, k = x.shape
+    if q8 is None:
+        q8 = _empty((m, k // 32, 36), torch.uint8, x.device, stream)
+    _check(lib().rz_q8_1_quant(_ptr(x), m, k, _ptr(q8), _stream(stream, x.device)))
+    return q8
+
+
+def rz_q8_q4k_gemm(q8, m: int, blocks, n: int, k: int, y=None, stream=None):
+    """-> y fp32 [m][n] = dequant(Q8_1 activation) @ dequant(Q4_K weight)^T."""
+    torch = _torch()
+    _require_cuda(q8, blocks, y)
+    if y is None:
+        y = _empty((m, n), torch.float32, blocks.device, stream)
+    _check(lib().rz_q8_q4k_gemm(_ptr(q8), m, _ptr(blocks), n, k, _ptr(y), _stream(stream, blocks.device)))
+    return y
 
 
 def rz_fp16_pack_weight(qtype: int, blocks, n: int, k: int, w_f16=None, stream=None):

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "librz_fp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "kquant.hip", "actquant.hip", "gemm.hip", "gemm_edge.hip", "kgemv.hip", "kqgemm.hip"]
+SOURCES = ["api.hip", "kquant.hip", "actquant.hip", "gemm.hip", "gemm_edge.hip", "kgemv.hip", "kqgemm.hip",
+           "q8gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -494,6 +494,40 @@ int rz_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32_t m, uint3
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
+size_t rz_q8_1_bytes(uint32_t m, uint32_t k) {
+    if (k == 0 || k % 256u != 0) return 0;
+    return (size_t)m * (k / 32u) * 36u;
+}
+
+int rz_q8_1_quant(const float* x, uint32_t m, uint32_t k, uint8_t* q8, void* stream) {
+    static const char* fn = "rz_q8_1_quant";
+    if (int r = check_k(fn, k)) return r;
+    if (m == 0) return RZ_OK;  // nothing to read or write
+    if (!x || !q8) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    if ((uint64_t)m * k > RZ_MAX_ELEMS) return fail(RZ_ERR_SHAPE, "%s: m*k too large", fn);
+    if (!aligned16(x) || !aligned16(q8)) return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_q8_1_quant(x, (uint64_t)m * k, q8, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
+int rz_q8_q4k_gemm(const uint8_t* q8, uint32_t m, const void* blocks, uint32_t n, uint32_t k, float* y,
+                   void* stream) {
+    static const char* fn = "rz_q8_q4k_gemm";
+    if (int r = check_k(fn, k)) return r;
+    if (m == 0 || n == 0) return RZ_OK;  // empty product: nothing to read or write
+    if (!q8 || !blocks || !y) return fail(RZ_ERR_NULL, "%s: null pointer", fn);
+    // the kernel addresses every operand and the output with 32-bit byte offsets
+    const uint64_t lim = 0xFFFFFF00ull;
+    if ((uint64_t)m * n * 4u > lim || (uint64_t)n * (k / 256u) * 144u > lim || (uint64_t)m * (k / 32u) * 36u > lim)
+        return fail(RZ_ERR_SHAPE, "%s: operand or output beyond 4 GB", fn);
+    if (!aligned16(q8) || !aligned16(blocks) || !aligned16(y))
+        return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    if (int r = check_device(fn)) return r;
+    hipError_t e = rz::launch_q8_q4k_gemm(q8, m, static_cast<const uint8_t*>(blocks), n, k, y, as_stream(stream));
+    return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
+}
+
 int rz_route_kquant_gemv(uint32_t m) { return m >= 1u && m <= RZ_KGEMV_ROUTE_MAX_M ? 1 : 0; }
 
 int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_dev, int qtype, const void* blocks,

@@ -85,6 +85,13 @@ hipError_t launch_encode(const float* x, uint64_t count, float scale, uint8_t* o
                          hipStream_t st);
 hipError_t launch_scales(const float* a, uint64_t count, float* q, float* dq, hipStream_t st);
 
+// ---- q8gemm.hip
+// Q8_1 blocks (36 bytes per 32 values) of `count` fp32 values (a multiple of 32).
+hipError_t launch_q8_1_quant(const float* x, uint64_t count, uint8_t* out, hipStream_t st);
+// y[m][n] = dequant(q8)[m][k] * dequant(Q4_K blocks)[n][k]^T.
+hipError_t launch_q8_q4k_gemm(const uint8_t* q8, uint32_t m, const uint8_t* blocks, uint32_t n, uint32_t k,
+                              float* y, hipStream_t st);
+
 // ---- kgemv.hip
 // y[m][n] = x[m][k] * dequant(blocks)^T for 1 <= m <= RZ_KGEMV_MAX_M.
 hipError_t launch_kquant_gemv(int qtype, const uint8_t* blocks, uint32_t n, uint32_t k, const float* x,

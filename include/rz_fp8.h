@@ -318,6 +318,46 @@ int rz_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float* act_scale_
                        void* stream);
 
 /* ---------------------------------------------------------------------
+ * Integer path: Q8_1 activation blocks times Q4_K weights (gemm.rs page,
+ * launch_dp4a_q4k_gemm and the DP4A_GEMM_PREFILL branch of
+ * cublas_prefill_gemm: the activation quantised to Q8_1, 36 bytes per 32
+ * values, then an 8-bit integer GEMM against the Q4_K blocks, fp32 out).
+ * --------------------------------------------------------------------- */
+
+/* Bytes of the Q8_1 form of an [m][k] activation: m * (k/32) * 36 (0 if k
+ * is not a positive multiple of 256). */
+size_t rz_q8_1_bytes(uint32_t m, uint32_t k);
+
+/*
+ * Q8_1 quantisation: for every 32 consecutive values x of a row, a =
+ * max |x| (NaN ignored), d = RN(a/127), id = RN(1/d) (0 when d == 0),
+ * q = the nearest integer to RN(x * id), halves away from zero, clamped to
+ * [-127, 127], 0 for a NaN product; the block is f16(d), f16(RN(d * sum q))
+ * (both to nearest even, little-endian), then the 32 codes as int8.
+ *   x   device, fp32 [m][k] row-major
+ *   q8  device out, rz_q8_1_bytes(m, k) bytes: row i is blocks i*(k/32) ...
+ * m == 0 is a no-op.  No workspace, no host synchronisation.
+ */
+int rz_q8_1_quant(const float* x, uint32_t m, uint32_t k, uint8_t* q8, void* stream);
+
+/*
+ * y[i][j] = sum_kk (f16(d)[i][kk/32] * q[i][kk]) * w[j][kk]   for i < m, j < n
+ * where the first factor is the Q8_1 value and w the exact Q4_K value
+ * d*sc*q4 - dmin*mn (as rz_dequant_f32 decodes it, before its fp32
+ * rounding).  Integer dot products of each 32-value sub-block on the
+ * matrix cores, scaled and accumulated in fp32.
+ *   q8      device, Q8_1 blocks of the activation (rz_q8_1_quant)
+ *   blocks  device, Q4_K weight [n][k], as for rz_fp8_pack_weight
+ *   y       device out, fp32 [m][n] row-major
+ * Q4_K only (the pages' integer path takes Q4_K weights).  m*n*4 bytes and
+ * both operands must each stay below 4 GB (RZ_ERR_SHAPE).  m == 0 or n == 0
+ * is a no-op.  No workspace, no host synchronisation.  Non-finite block
+ * scales give non-finite outputs.
+ */
+int rz_q8_q4k_gemm(const uint8_t* q8, uint32_t m, const void* blocks, uint32_t n, uint32_t k, float* y,
+                   void* stream);
+
+/* ---------------------------------------------------------------------
  * FP16 comparator: the cached-fp16-weight GEMM the FP8 path replaced
  * (gemm.rs page, get_or_cache_fp16_weight and cublas_prefill_hgemm; mod.rs
  * page, F32_TO_F16_PTX and the module note on the tensor-core speed-up).
