@@ -38,6 +38,10 @@ blocks, FP8 GEMM, activation quantisation + FP8 GEMM) at N=4608, K=3584.
 cache, fp16 activation, fp16 MFMA GEMM) beside the FP8 path on the FFN
 shapes at M=2048, with both paths' accuracy on the gate GEMM.
 
+--q8-gemm instead times the integer path (Q8_1 activation blocks x Q4_K
+weight on the int8 matrix cores) beside the FP8 path, with both paths'
+accuracy on the gate GEMM.
+
 --kquant-gemm instead times the FP8 GEMM that encodes the weight from its
 K-quant blocks inside the kernel (no FP8 weight cache) beside the cached
 path's GEMM, at the model's prefill shapes (warm).
@@ -516,6 +520,79 @@ def fp16_gemm(args, dev) -> int:
     return 0
 
 
+# The integer path's vector-ALU bound: every output takes three ALU operations
+# per 32-value sub-block (convert the integer block sum, form the scale
+# product, fused multiply-add), i.e. 3/32 operation per multiply-add, on
+# 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz (non-packed fp32).
+INT_PATH_ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * (32 / 3) * 2 / 1e12
+
+
+def q8_gemm(args, dev) -> int:
+    """The integer path (Q8_1 activation x Q4_K weight) beside the FP8 path
+    on the FFN gate/up shape at M=2048 and M=4096 and the attention Q shape
+    (one line): warm times, HIP events around 20 launches after 5 warm-up
+    launches, and the accuracy of both paths' outputs on 64 rows against a
+    float64 product of the fp32 activation and the fp32 dequantised weight
+    (torch float64 on the GPU, from rz_dequant_f32)."""
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=20):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    rows = {}
+    for name, m, n, k in [("cfg3 gate/up", 2048, 18944, 3584), ("cfg4 gate/up", 4096, 18944, 3584),
+                          ("cfg2 q", 512, 3584, 3584)]:
+        x = torch.from_numpy(W.act_normal(41 + m, m, k)).to(dev)
+        blocks = torch.from_numpy(W.q4k_blocks(42 + n, n, k)).to(dev)
+        q8 = rz.rz_q8_1_quant(x, stream=stream)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        t_q = timed(lambda: rz.rz_q8_1_quant(x, q8, stream))
+        t_g = timed(lambda: rz.rz_q8_q4k_gemm(q8, m, blocks, n, k, y, stream))
+        a8, sc = rz.rz_fp8_quant_act(x, stream=stream)
+        w8, scale, _ = rz.rz_fp8_pack_weight(W.Q4_K, blocks, n, k, stream=stream)
+        y8 = torch.empty((m, n), dtype=torch.float32, device=dev)
+        t_f = timed(lambda: rz.rz_fp8_gemm(a8, w8, m, sc, scale, y8, stream, ws=None))
+        fl = 2.0 * m * n * k
+        rows[name] = {"m": m, "n": n, "k": k, "q8_quant_us": round(t_q * 1e6, 1),
+                      "q8_gemm_us": round(t_g * 1e6, 1), "q8_gemm_tops": round(fl / t_g / 1e12, 1),
+                      "fp8_gemm_us": round(t_f * 1e6, 1), "fp8_gemm_tflops": round(fl / t_f / 1e12, 1)}
+        if name == "cfg3 gate/up":
+            wf = rz.rz_dequant_f32(W.Q4_K, blocks, n, k, stream=stream)
+            sel = torch.linspace(0, m - 1, 64, device=dev).long()
+            ref = x[sel].double() @ wf.double().t()
+            den = ref.abs().mean().item()
+            rows[name]["accuracy_vs_fp64_of_fp32_inputs"] = {
+                nm: {"mean_abs_err_rel": round((yy[sel].double() - ref).abs().mean().item() / den, 6),
+                     "max_abs_err_rel": round((yy[sel].double() - ref).abs().max().item() / den, 6)}
+                for nm, yy in (("q8_1 x q4_k", y), ("fp8", y8))}
+            del wf, ref
+        log(f"{name}: {rows[name]}")
+        del x, blocks, q8, y, a8, w8, y8
+    g = rows["cfg3 gate/up"]
+    ach = 2.0 * g["m"] * g["n"] * g["k"] / (g["q8_gemm_us"] * 1e-6) / 1e12
+    roof = {"kernel": "q8_q4k_gemm_kernel (M=2048, N=18944, K=3584)", "bound": "alu", "achieved": round(ach, 1),
+            "peak": round(INT_PATH_ALU_PEAK_TOPS, 1), "unit": "TOPS", "frac": round(ach / INT_PATH_ALU_PEAK_TOPS, 4),
+            "int8_mfma_peak_tops": 5000.0, "frac_of_int8_mfma_peak": round(ach / 5000.0, 4), "traffic": None}
+    out = {"metric": "Q8_1 x Q4_K integer GEMM vs FP8 GEMM (warm)", "unit": "us", "higher_is_better": False,
+           "rows": rows, "roofline": roof, "dtype": "int8 x 4-bit (int32 block sums, fp32 accumulate)",
+           "data": "synthetic", "config": {"workload": "prefill GEMM shapes of the 7B-class model, Q4_K weights"}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,6 +611,8 @@ def main() -> int:
                     help="instead time the small-batch paths at N=4608, K=3584 (Q4_K) for these m")
     ap.add_argument("--fp16-gemm", action="store_true",
                     help="instead time the FP16 cached-weight comparator beside the FP8 path (warm, M=2048 FFN)")
+    ap.add_argument("--q8-gemm", action="store_true",
+                    help="instead time the integer path (Q8_1 activation x Q4_K weight) beside the FP8 path (warm)")
     ap.add_argument("--kquant-gemm", action="store_true",
                     help="instead time the GEMM straight from K-quant blocks beside the cached path (warm)")
     args = ap.parse_args()
@@ -572,6 +651,8 @@ def main() -> int:
         return kquant_gemm(args, dev)
     if args.fp16_gemm:
         return fp16_gemm(args, dev)
+    if args.q8_gemm:
+        return q8_gemm(args, dev)
     if args.small_m is not None:
         if not args.small_m:
             args.small_m = [1, 2, 3, 4, 8, 37]

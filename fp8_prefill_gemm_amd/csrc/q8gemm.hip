@@ -162,6 +162,14 @@ __global__ __launch_bounds__(kThreads, 2) void q8_q4k_gemm_kernel(const uint8_t*
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
 
+    // activation fragments of the current sub-block, loaded one sub-block ahead
+    v4i an[2];
+    uint32_t dn[2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+        an[tm] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, arow[tm] + 4u + 16u * h, 0, 0));
+        dn[tm] = __builtin_amdgcn_raw_buffer_load_b32(ars, arow[tm], 0, 0);
+    }
     for (int sb = 0; sb < nsb; ++sb) {
         // the lanes' weight rows: header and the four 16-byte quant slices of this half
         float tp[2][8], mp[2][8];
@@ -190,14 +198,23 @@ __global__ __launch_bounds__(kThreads, 2) void q8_q4k_gemm_kernel(const uint8_t*
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
                 const int j = 2 * c + hi;
-                const uint32_t blk = (uint32_t)(sb * 8 + j) * kQ8Block;
                 v4i a[2];
                 float d8[2];
 #pragma unroll
                 for (int tm = 0; tm < 2; ++tm) {
-                    a[tm] = __builtin_bit_cast(
-                        v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, arow[tm] + blk + 4u + 16u * h, 0, 0));
-                    d8[tm] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b32(ars, arow[tm] + blk, 0, 0) & 0xFFFFu);
+                    a[tm] = an[tm];
+                    d8[tm] = half_bits_to_float(dn[tm] & 0xFFFFu);
+                }
+                // the next sub-block's activation fragments (the first of the next
+                // super-block after j = 7; past the end they read zero, unused)
+                {
+                    const uint32_t nblk = (uint32_t)(sb * 8 + j + 1) * kQ8Block;
+#pragma unroll
+                    for (int tm = 0; tm < 2; ++tm) {
+                        an[tm] = __builtin_bit_cast(
+                            v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, arow[tm] + nblk + 4u + 16u * h, 0, 0));
+                        dn[tm] = __builtin_amdgcn_raw_buffer_load_b32(ars, arow[tm] + nblk, 0, 0);
+                    }
                 }
                 v4i b[2];
 #pragma unroll
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void q8_q4k_gemm_kernel(const uint8_t*
                     int s = code_sum(a[tm]);
                     s += __shfl_xor(s, 32, 64);
                     sig[tm][hi] = d8[tm] * (float)s;  // exact (11 + 12 bits)
-                    if (h == 0) tab[tm * 32 + r] = d8[tm];
+                    tab[tm * 32 + r] = d8[tm];  // both half-waves write the same value
                 }
                 __builtin_amdgcn_wave_barrier();
                 float rs[2][16];
@@ -235,12 +252,17 @@ __global__ __launch_bounds__(kThreads, 2) void q8_q4k_gemm_kernel(const uint8_t*
                     }
             }
             // the min term of sub-blocks 2c, 2c+1: rows supply f16(d8)*S, columns -dmin*mn
+            float mpv[2], sgv[2];  // this lane's K index of the pair (h): two-way selects
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                mpv[i] = h ? mp[i][2 * c + 1] : mp[i][2 * c];
+                sgv[i] = h ? sig[i][1] : sig[i][0];
+            }
 #pragma unroll
             for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < 2; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? sig[tm][1] : sig[tm][0],
-                                                                       mp[tn][2 * c + h], acc[tm][tn], 0, 0, 0);
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(sgv[tm], mpv[tn], acc[tm][tn], 0, 0, 0);
         }
     }
     // acc[tm][tn][e]: row m0 + 32tm + 8(e/4) + 4h + e%4, column n0 + 32tn + r
