@@ -507,7 +507,7 @@ def fp16_gemm(args, dev) -> int:
     g = rows["gate"]
     ach = 2.0 * g["m"] * g["n"] * g["k"] / (g["fp16_gemm_us"] * 1e-6) / 1e12
     plan = rz.rz_fp8_gemm_plan(g["m"], g["n"], 2 * g["k"])
-    roof = {"kernel": f"fp8_gemm_interior_kernel<fp16 operands>, {plan[0]}x{plan[1]} tiles, {plan[3]} workgroups "
+    roof = {"kernel": f"fp8_gemm_interior_kernel<fp16 operands>, {plan[0]}x{plan[1]} tiles, {plan[3]} persistent workgroups "
                       "(M=2048, N=18944, K=3584)",
             "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0, "unit": "TFLOP/s",
             "frac": round(ach / 2500.0, 4), "traffic": None}
@@ -791,7 +791,7 @@ def main() -> int:
             "m": M, "gate_up": [gate.n, gate.k], "down": [dn.n, dn.k],
         },
         "roofline": {
-            "kernel": (f"gate+up GEMM in one launch, {plan[0]}x{plan[1]} tiles, {plan[3]} workgroups "
+            "kernel": (f"gate+up GEMM in one launch, {plan[0]}x{plan[1]} tiles, {plan[3]} persistent workgroups "
                        f"(M=2048, N=2x18944, K=3584)"),
             "bound": "mfma",
             "achieved": round(achieved, 2),

@@ -564,7 +564,7 @@ int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out) {
     cfg_out[0] = p.bn;
     cfg_out[1] = p.bm;
     cfg_out[2] = p.threads;
-    cfg_out[3] = (m == 0 || n == 0) ? 0 : p.workgroups + p.half_workgroups;
+    cfg_out[3] = (m == 0 || n == 0) ? 0 : p.workgroups;
     return RZ_OK;
 }
 

@@ -169,19 +169,15 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
 }
 
 // ---------------------------------------------------------------------------
-// Interior 256x256 tiles.
+// Interior 256x256 tiles: a persistent kernel.
 //
 // The output splits into T = tiles_m * tiles_n tiles of 256 x 256
 // (tiles_m = ceil(padded M / 256), tiles_n = ceil(N / 256); see the kernel
-// for the last tile when padded M or N is not a multiple of 256).  G = one workgroup per CU; the
-// first R*G tiles (R = floor(T/G) full rounds, chosen as whole n-columns of
-// tiles) run one tile per workgroup.  The rem = T - R*G tiles left over
-// would leave most CUs idle for a whole tile time; when their n-columns cut
-// into half tiles of 128 activation rows (ceil(padded M / 128) per column)
-// fit one round, those run as workgroups after the whole tiles in the same
-// launch, so the last round takes about half a tile time.  A half tile runs
-// the whole K range and stores its own output: no partial sums, no
-// workspace, no workgroup waits for another.
+// for the last tile when padded M or N is not a multiple of 256).  The
+// 128 KB of LDS leave room for one workgroup per CU, so the grid is one
+// workgroup per CU, W per XCD, and each workgroup runs a list of tiles.
+// A tile runs the whole K range and stores its own output: no partial sums,
+// no workspace, no workgroup waits for another.
 //
 // The K loop (tile_mainloop): two LDS slots, the global loads three K-steps
 // ahead of the MFMAs in two register sets.
@@ -268,36 +264,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
     return __builtin_amdgcn_make_buffer_rsrc(Y + (size_t)m0 * N, (short)0, rows * N * 4, 0x00020000);
 }
 
-// Work of the interior-tile kernel.  The grid is nwhole whole-tile
-// workgroups followed by the half tiles.
-//   Whole tiles: the first nd n-columns of tiles (all m), in the grouped
-//   order (groups of group_m m-tiles).  The dispatcher sends workgroup w to
-//   XCD w % 8, so XCD x is given the contiguous range [x*T/8, (x+1)*T/8) of
-//   that order: the workgroups that run together on one XCD share weight
-//   and activation rows through its L2.
-//   Half tiles: n-columns [nd, tiles_n) by halves_m activation halves of
-//   128 rows, nhalf of them in a grouped order with groups of half_gm
-//   halves; XCD x again takes a contiguous range of that order.
+// Work of the interior-tile kernel.  The dispatcher sends workgroup w to
+// XCD w % 8; workgroup j = w / 8 of XCD x (j < W) works on a contiguous
+// run of the T tiles in the grouped order (groups of group_m m-tiles, m
+// fastest inside a group), Tx of them, so the workgroups that run together
+// on one XCD share weight and activation rows through its L2:
+//   R = Tx / W whole rounds: tile r*W + j of the run in round r;
+//   the L = Tx - R*W tiles left over run as half tiles of 128 activation
+//   rows when a whole round comes before them or their 2L halves fit one
+//   round (else as whole tiles, one each for workgroups j < L).
+// Half tiles go out in half_rank order (the odd workgroups first), and an
+// odd workgroup runs its first half tile before its whole tiles, an even
+// one after them: the two halves of an XCD then reach the end of their
+// whole tiles half a tile apart.  Measured on the 256x256 tiles, the 256 KB
+// output store of a tile takes ~7k cycles when 16 CUs of an XCD store
+// together and ~16k when all 32 do, whether or not the other XCDs store at
+// the same time (the XCD's write path is the limit, not HBM).
 // When the padded M (mp, a multiple of 16) is not a multiple of the tile
 // height, the last m-tile (half) starts at mp - 256 (mp - 128) instead, and
 // when N is not a multiple of 256 the last n-tile starts at N - 256: such a
 // tile overlaps the one before it, so every row it loads exists and every
 // column it stores is < N, and the outputs both compute get the same
-// operands in the same order, so both store the same values there.
+// operands in the same order, so both store the same values there.  Every
+// output element is so computed over the whole K in one order, whichever
+// workgroup runs it: the results do not depend on the CU count or on which
+// GEMMs share a launch.
 struct InteriorPlan {
-    int tiles_m, tiles_n, nd, nwhole, group_m;
-    int halves_m, nhalf, half_gm;
+    int tiles_m, tiles_n, group_m, T, W;
 };
 
-// Contiguous share of XCD x (workgroup w) of T items in order; false if w
-// has none.
-__device__ __forceinline__ bool xcd_item(int w, int T, int& t) {
-    const int tall = T / kXcds, rem = T % kXcds;
-    const int x = w % kXcds, loc = w / kXcds;
-    if (loc >= tall + (x < rem ? 1 : 0)) return false;
-    t = x * tall + (x < rem ? x : rem) + loc;
-    return true;
-}
+// XCD-local rank of workgroup j in the hand-out order of half tiles: the
+// odd workgroups first, then the even ones.
+__device__ __forceinline__ int half_rank(int j, int W) { return (j & 1) ? (j >> 1) : (W >> 1) + (j >> 1); }
 
 // The weight and output of the n-tile starting at column n0 of the launch:
 // the launch's N columns are the groups' columns one after the other (every
@@ -322,44 +320,77 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][512 * kBK];
 
     const int bid = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int wn = wid & 1, wm = wid >> 1;
-    const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
     const uint32_t step = 32u * (uint32_t)K;
     const float act_dq = F16 ? 1.0f : act_scale[1];
     const int mp = (M + 15) & ~15;  // >= 256 here
-    int t, n0, m0;
-    if (bid < P.nwhole) {
-        (void)xcd_item(bid, P.nwhole, t);
-        grouped_origin_bb<256, 256>(t, P.tiles_m, P.nd, P.group_m, n0, m0);
-        m0 = m0 < mp - 256 ? m0 : mp - 256;
+    const int x = bid % kXcds, j = bid / kXcds;
+    const int tall = P.T / kXcds, trem = P.T % kXcds;
+    const int first = x * tall + (x < trem ? x : trem);
+    const int Tx = tall + (x < trem ? 1 : 0);
+    const int R = Tx / P.W, L = Tx - R * P.W;
+    const bool halves = R > 0 || 2 * L <= P.W;
+    const int H = halves ? 2 * L : 0;  // half tiles of this XCD
+    const int hr = half_rank(j, P.W);
+    // items in order: [half hr if j is odd] [whole rounds] [the left-over
+    // whole tile j] [halves hr (j even), hr + W, hr + 2W, ...]
+    const bool early = (j & 1) && hr < H;
+    int idx = early ? -1 : 0;  // -1: the early half; 0..R-1: rounds; R: left-over whole tile
+    int hnext = early ? hr + P.W : hr;
+    for (;;) {
+        bool half = false;
+        int lt, mh = 0;  // tile of the XCD's run, activation half
+        if (idx < 0) {
+            half = true;
+            lt = R * P.W + hr / 2;
+            mh = hr & 1;
+            idx = 0;
+        } else if (idx < R) {
+            lt = idx * P.W + j;
+            ++idx;
+        } else if (idx == R && !halves && j < L) {
+            lt = R * P.W + j;
+            ++idx;
+        } else if (hnext < H) {
+            half = true;
+            lt = R * P.W + hnext / 2;
+            mh = hnext & 1;
+            hnext += P.W;
+        } else {
+            break;
+        }
+        // the per-lane values are rebuilt from an opaque copy of the thread
+        // id for every tile, so that the compiler keeps none of them (nor
+        // the addresses made from them) live across the tile loop
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wid = tid >> 6;
+        const int wn = wid & 1, wm = wid >> 1;
+        const uint32_t voff = (uint32_t)(tid >> 3) * (uint32_t)K + 16u * (uint32_t)(tid & 7);
+        int n0, m0;
+        grouped_origin_bb<256, 256>(first + lt, P.tiles_m, P.tiles_n, P.group_m, n0, m0);
         n0 = n0 < N - 256 ? n0 : N - 256;
         int Ng;
         const int g = group_of(G, n0, Ng);
-        const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
-        v16f acc[4][4];
-        tile_mainloop<4, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
-                         tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
-        store_acc<4>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
-                     act_dq * G.w_scale[g]);
-        return;
+        if (!half) {
+            m0 = m0 < mp - 256 ? m0 : mp - 256;
+            const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
+            v16f acc[4][4];
+            tile_mainloop<4, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
+                                  tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
+            store_acc<4>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
+                         act_dq * G.w_scale[g]);
+        } else {
+            m0 += 128 * mh;
+            m0 = m0 < mp - 128 ? m0 : mp - 128;
+            const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
+            v16f acc[4][2];
+            tile_mainloop<2, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
+                                  tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
+            store_acc<2>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
+                         act_dq * G.w_scale[g]);
+        }
     }
-    // nwhole is a multiple of 8: the half tiles' workgroups keep w % 8
-    if (!xcd_item(bid - P.nwhole, P.nhalf, t)) return;
-    grouped_origin_bb<256, 128>(t, P.halves_m, P.tiles_n - P.nd, P.half_gm, n0, m0);
-    m0 = m0 < mp - 128 ? m0 : mp - 128;
-    n0 += P.nd * 256;
-    n0 = n0 < N - 256 ? n0 : N - 256;
-    int Ng;
-    const int g = group_of(G, n0, Ng);
-    const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
-    v16f acc[4][2];
-    tile_mainloop<2, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
-                     tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
-    store_acc<2>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
-                 act_dq * G.w_scale[g]);
 }
 
 struct KindInfo {
@@ -397,9 +428,10 @@ int edge_split(int kind, int mp, uint32_t n, uint32_t k) {
 //    pages also route M < 4 to their GEMV path);
 //  * the skinny kernel (16 weight rows per workgroup, K split over its
 //    waves) when padded M <= 64;
-//  * interior 256x256 tiles (whole-tile rounds, then the tiles left over
-//    as half tiles when they fit one round) when N and padded M are
-//    >= 256, K >= 512, N < 2^21 and there are at least 64 tiles;
+//  * the persistent interior kernel (256x256 tiles in rounds, the tiles
+//    left over as half tiles; one workgroup per CU) when N and padded M
+//    are >= 256, K >= 512, N < 2^21, there are at least 64 tiles and the
+//    CUs split evenly over the 8 XCDs, at least 2 on each;
 //  * 256x256 edge-capable kernel when padded M < 256 but there are still
 //    >= 256 tiles;
 //  * 128x128 tiles when M_pad >= 128 and tiles times K chunks give >= 128
@@ -411,23 +443,11 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     GemmPlan p = {};
     p.s = 1;
     const int t256 = ceil_div(mp, 256) * ceil_div((int)n, 256);
-    if (mp >= 256 && n >= 256u && k >= 512u && n < (1u << 21) && t256 >= 64 && cus % kXcds == 0) {
+    if (mp >= 256 && n >= 256u && k >= 512u && n < (1u << 21) && t256 >= 64 && cus % kXcds == 0 &&
+        cus / kXcds >= 2) {
         p.kind = kGemmTiles;
         p.G = cus;
-        const int tiles_m = ceil_div(mp, 256);
-        p.R = t256 / cus;
-        // the whole-tile rounds must be whole n-columns of tiles
-        if ((p.R * cus) % tiles_m != 0) p.R = 0;
-        p.rem = t256 - p.R * cus;
-        const int nhalf = ceil_div(mp, 128) * (p.rem / tiles_m);  // halves of the leftover n-columns
-        if (p.rem > 0 && nhalf <= cus) {  // last round in half tiles
-            p.workgroups = p.R * cus;
-            p.half_workgroups = kXcds * ceil_div(nhalf, kXcds);
-        } else {  // every tile whole
-            p.R = t256 / cus;
-            p.rem = 0;
-            p.workgroups = t256;
-        }
+        p.workgroups = cus;  // persistent: one workgroup per CU
     } else if (m <= 3) {
         p.kind = kGemmGemv;
     } else if (mp <= 64) {
@@ -506,27 +526,16 @@ hipError_t launch_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32
 hipError_t launch_interior(const GemmPlan& p, const uint8_t* a_fp8, const GemmGroups& G, uint32_t m, uint32_t n,
                            uint32_t k, const float* act_scale, hipStream_t st, bool f16) {
     const int mp = (int)((m + 15u) & ~15u);
-    const int tiles_m = ceil_div(mp, 256);
     InteriorPlan ip;
-    ip.tiles_m = tiles_m;
+    ip.tiles_m = ceil_div(mp, 256);
     ip.tiles_n = ceil_div((int)n, 256);
-    ip.nwhole = p.workgroups;  // whole tiles: the first n-columns (all of them without halves)
-    ip.nd = p.workgroups / tiles_m;
-    ip.group_m = tiles_m < 8 ? tiles_m : 8;
-    ip.halves_m = ceil_div(mp, 128);
-    ip.nhalf = ip.halves_m * (p.rem / tiles_m);
-    // groups of about sqrt(2 * halves per XCD) halves: each XCD's block of
-    // half tiles is near square in elements
-    const int per_xcd = ceil_div(ip.nhalf, kXcds);
-    int hgm = 1;
-    while (hgm * 2 <= ip.halves_m && hgm * hgm * 2 <= per_xcd) hgm *= 2;
-    ip.half_gm = hgm;
+    ip.group_m = ip.tiles_m < 8 ? ip.tiles_m : 8;
+    ip.T = ip.tiles_m * ip.tiles_n;
+    ip.W = p.G / kXcds;
     if (f16)
-        fp8_gemm_interior_kernel<true><<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n,
-                                                                                      (int)k, act_scale, ip);
+        fp8_gemm_interior_kernel<true><<<p.workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n, (int)k, act_scale, ip);
     else
-        fp8_gemm_interior_kernel<false><<<p.workgroups + p.half_workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n,
-                                                                                       (int)k, act_scale, ip);
+        fp8_gemm_interior_kernel<false><<<p.workgroups, 256, 0, st>>>(a_fp8, G, (int)m, (int)n, (int)k, act_scale, ip);
     return hipGetLastError();
 }
 

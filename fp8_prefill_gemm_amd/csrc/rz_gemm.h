@@ -12,11 +12,10 @@ namespace rz {
 enum GemmKind { kGemmTiles = 0, kGemmMedium = 1, kGemmSmall = 2, kGemmLargeEdge = 3, kGemmSkinny = 4, kGemmGemv = 5 };
 struct GemmPlan {
     int bn, bm, threads, workgroups, kind;
-    // interior-tile plan: CUs, whole-tile rounds, tiles left over (run as
-    // half tiles), workgroups for those half tiles
-    int G, R, rem, half_workgroups;
-    // edge-capable plans: K chunks per tile (1: no split)
-    int s;
+    // interior-tile plan: CUs (the persistent grid, one workgroup each)
+    int G;
+    // edge-capable plans: tiles, K chunks per tile (1: no split)
+    int rem, s;
     size_t ws_bytes;  // workspace the plan needs (0: none)
 };
 GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allowed);

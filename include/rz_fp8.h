@@ -426,8 +426,10 @@ int rz_fp8_scales(const float* absmax_dev, uint64_t count, float* q_out_dev,
 
 /* GEMM tile configuration rz_fp8_gemm would launch for this shape (with a
  * large enough workspace): writes {BN, BM, threads, workgroups} to
- * cfg_out[4] (host); workgroups is the grid of the one launch: whole tiles
- * plus half tiles, or tiles times K chunks when K is split. */
+ * cfg_out[4] (host); workgroups is the grid of the one launch: one per
+ * compute unit for the persistent 256x256 kernel (which also runs half
+ * tiles of 128 activation rows), otherwise tiles, or tiles times K chunks
+ * when K is split. */
 int rz_fp8_gemm_plan(uint32_t m, uint32_t n, uint32_t k, int32_t* cfg_out);
 
 const char* rz_status_string(int status);

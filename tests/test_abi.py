@@ -275,7 +275,7 @@ def test_plans_cover_shapes(L):
         tiles = -(-mp // bm) * -(-n // bn)
         interior = (bn, bm) == (256, 256) and mp >= 256 and 256 <= n < 1 << 21 and k >= 512 and tiles >= 64
         if interior:
-            assert wgs == _interior_wgs(mp, -(-n // 256), k)
+            assert wgs == 256  # persistent: one workgroup per CU
         else:
             assert (bn, bm, wgs) == _edge_plan(m, n, k)[:3]
             assert wgs >= tiles
@@ -314,33 +314,67 @@ def _edge_plan(m, n, k, cus=256):
     return bn, bm, 8 * -(-t // 8) * s, -(-4 * t // 256) * 256 + t * s * bn * bm * 4
 
 
-def _interior_wgs(mp, tiles_n, k, cus=256):
-    """Workgroups of an interior-tile plan (256 CUs without a device) for a
-    padded M of mp rows: whole 256x256 tiles (ceil(mp/256) per n-column) for
-    the full rounds (whole n-columns of tiles, else none), then the leftover
-    n-columns as half tiles of 128 rows (ceil(mp/128) per column) when those
-    fit one round (rounded up to a multiple of 8 XCDs), or every tile whole."""
-    tiles_m = -(-mp // 256)
-    t = tiles_m * tiles_n
-    r = t // cus
-    if (r * cus) % tiles_m:
-        r = 0
-    rem = t - r * cus
-    nhalf = -(-mp // 128) * (rem // tiles_m)
-    if 0 < rem and nhalf <= cus:
-        return r * cus + 8 * -(-nhalf // 8)
-    return t
+def _interior_items(T, W):
+    """Per-workgroup item lists of the persistent interior kernel, as the
+    kernel builds them: XCD x (workgroups w with w % 8 == x, j = w // 8)
+    takes a contiguous run of Tx tiles; R = Tx // W whole rounds (tile
+    r*W + j), the L left over as 2L half tiles when R > 0 or 2L <= W (else
+    whole, one per workgroup j < L); halves handed out odd workgroups first,
+    an odd one running its first half before its whole tiles.
+    -> {(x, j): [("w", tile) | ("h", tile, half)]}"""
+    out = {}
+    tall, trem = divmod(T, 8)
+    for x in range(8):
+        first = x * tall + min(x, trem)
+        tx = tall + (1 if x < trem else 0)
+        r, l = divmod(tx, W)
+        halves = r > 0 or 2 * l <= W
+        h = 2 * l if halves else 0
+        for j in range(W):
+            hr = j // 2 if j % 2 else W // 2 + j // 2
+            items = []
+            early = j % 2 == 1 and hr < h
+            if early:
+                items.append(("h", first + r * W + hr // 2, hr % 2))
+            items += [("w", first + i * W + j) for i in range(r)]
+            if not halves and j < l:
+                items.append(("w", first + r * W + j))
+            for q in range(hr + (W if early else 0), h, W):
+                items.append(("h", first + r * W + q // 2, q % 2))
+            out[(x, j)] = items
+    return out
 
 
 def test_interior_plan_examples(L):
-    # FFN gate/up at M=2048: 2 full rounds of whole tiles + 80 tiles as 160 half tiles
-    assert rz.rz_fp8_gemm_plan(2048, 18944, 3584)[3] == 512 + 160
-    # FFN down at M=2048: 112 tiles, all as 224 half tiles
-    assert rz.rz_fp8_gemm_plan(2048, 3584, 18944)[3] == 224
-    # M=4096: 1184 tiles, the 160 left over make 320 halves, more than a round: all whole
-    assert rz.rz_fp8_gemm_plan(4096, 18944, 3584)[3] == 1184
-    # 3 m-tiles: 256-tile rounds are not whole n-columns, 300 tiles all whole
-    assert rz.rz_fp8_gemm_plan(768, 25600, 512)[3] == 300
+    # the persistent interior kernel: one workgroup per CU (256 without a device)
+    for m, n, k in [(2048, 18944, 3584), (2048, 3584, 18944), (4096, 18944, 3584), (768, 25600, 512),
+                    (2048, 37888, 3584)]:
+        assert rz.rz_fp8_gemm_plan(m, n, k)[:4] == (256, 256, 256, 256)
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(8, 74), (8, 148), (8, 14), (16, 14), (16, 148), (3, 100), (2, 74),
+                                             (1, 64), (8, 32), (5, 13)])
+def test_interior_schedule_covers_tiles_once(tiles_m, tiles_n):
+    W = 32
+    T = tiles_m * tiles_n
+    items = _interior_items(T, W)
+    seen = {}
+    for lst in items.values():
+        for it in lst:
+            key = (it[1], it[2]) if it[0] == "h" else (it[1], None)
+            seen[key] = seen.get(key, 0) + 1
+    assert all(v == 1 for v in seen.values())
+    for t in range(T):  # whole, or both halves
+        assert ((t, None) in seen) != ((t, 0) in seen and (t, 1) in seen)
+        assert ((t, 0) in seen) == ((t, 1) in seen)
+    # load in half-tile units: at most one tile above the average
+    load = {wj: sum(2 if it[0] == "w" else 1 for it in lst) for wj, lst in items.items()}
+    assert max(load.values()) <= -(-2 * T // (8 * W)) + 2
+    # with whole rounds and half tiles, every odd workgroup that has a half runs it first
+    for (x, j), lst in items.items():
+        if j % 2 and any(it[0] == "h" for it in lst) and any(it[0] == "w" for it in lst):
+            assert lst[0][0] == "h"
+
 
 
 def test_binding_refuses_host_tensors(L):

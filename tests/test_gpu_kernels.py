@@ -311,36 +311,40 @@ def _codes(g, shape):
     return a | (g.integers(0, 2, size=shape) << 7).astype(np.uint8)
 
 
+# The persistent interior kernel (256 CUs, 32 per XCD): XCD x runs a
+# contiguous run of Tx tiles, R = Tx // 32 whole rounds and the L tiles left
+# over as 2L half tiles when R > 0 or 2L <= 32, else as L whole tiles.
 @pytest.mark.parametrize("m,n,k,full", [
-    (2048, 2560, 1536, True),    # 80 tiles: all as 160 half tiles
+    (2048, 2560, 1536, True),    # 80 tiles, 10 per XCD: all as half tiles
     (2040, 2560, 1024, True),    # same with M padded to 2048: rows >= M dropped
-    (2048, 2560, 768, True),     # 80 tiles as half tiles, 6 K-steps
-    (2048, 3584, 1024, True),    # 112 tiles: 224 half tiles
-    (2048, 10240, 1024, False),  # 320 tiles: one whole round + 64 tiles as halves
-    (2048, 8960, 512, False),    # 280 tiles: one whole round + 24 tiles as halves
+    (2048, 2560, 768, True),     # half tiles only, 6 K-steps
+    (2048, 3584, 1024, True),    # 112 tiles: 28 half tiles per XCD
+    (2048, 10240, 1024, False),  # 320 tiles: one whole round + 8 tiles per XCD as halves
+    (2048, 8960, 512, False),    # 280 tiles: 35 per XCD, one round + 3 tiles as halves
     (4096, 4096, 512, False),    # 256 tiles: exactly one round
-    (4096, 4608, 1024, False),   # 288 tiles: one round + 32 tiles as halves
-    (768, 25600, 512, False),    # 300 tiles, rounds not whole n-columns: all whole
+    (4096, 4608, 1024, False),   # 288 tiles: one round + 4 tiles per XCD as halves
+    (4096, 3584, 1024, False),   # 224 tiles, 28 per XCD: no round, the 56 halves would not fit one: whole
+    (768, 25600, 512, False),    # 300 tiles, 37 or 38 per XCD: one round + halves
     (2040, 3584, 4864, False),   # 112 tiles as half tiles with long K, rows >= M dropped
     # padded M not a multiple of 256: the last m-tile (half) is moved up to
     # end at the last activation row and overlaps the one before it
-    (2000, 18944, 512, False),   # 2 rounds + 10 n-columns of 16 halves; last tile at 1744, half at 1872
-    (1900, 2560, 1024, True),    # halves only, 15 per n-column (the last at 1776)
-    (300, 16384, 512, False),    # 3 halves per n-column: 0, 128 and 176
-    (600, 25600, 512, False),    # 300 whole tiles, the last m-tile at 352
-    (1000, 65536, 512, False),   # 4 whole rounds, the last m-tile at 752
+    (2000, 18944, 512, False),   # 2 rounds + halves; last tile at 1744, half at 1872
+    (1900, 2560, 1024, True),    # halves only (the last at 1776)
+    (300, 16384, 512, False),    # 128 tiles: halves at 0, 128 and 176
+    (300, 18944, 512, False),    # 148 tiles, 18 or 19 per XCD: whole tiles, the last m-tile at 48
+    (600, 25600, 512, False),    # 300 tiles, one round + halves, the last m-tile at 352
+    (1000, 65536, 512, False),   # 4 whole rounds, nothing left over, the last m-tile at 752
     # N not a multiple of 256: the last n-tile starts at N - 256
     (2048, 2500, 1024, True),    # halves only; last n-tile at 2244
     (2000, 18900, 512, False),   # ragged M and N: 2 rounds + halves, last tile at (1744, 18644)
-    (768, 25700, 512, False),    # 303 whole tiles, the last n-tile at 25444
-    (1000, 40000, 512, False),   # 2 rounds + 29 n-columns of 8 halves, ragged M and N
+    (768, 25700, 512, False),    # 303 tiles, one round + halves, the last n-tile at 25444
+    (1000, 40000, 512, False),   # 2 rounds + halves, ragged M and N
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
-    from tests.test_abi import _interior_wgs
     mp = fp8_path.pad_m(m)
     bn, bm, threads, wgs = rz.rz_fp8_gemm_plan(m, n, k)
     assert (bn, bm, threads) == (256, 256, 256)
-    assert wgs == _interior_wgs(mp, -(-n // 256), k)
+    assert wgs == torch.cuda.get_device_properties(0).multi_processor_count  # one per CU
     assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) == 0
     g = np.random.Generator(np.random.PCG64(m + n + k))
     a8, w8 = _codes(g, (mp, k)), _codes(g, (n, k))
