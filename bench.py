@@ -63,6 +63,7 @@ METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock.json")
 KGEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kgemv_traffic.json")
 KGEMV_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f) for f in ("kgemv.hip", "rz_device.h")]
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_prefill_gemm_amd", "csrc", f)
@@ -93,6 +94,24 @@ def measured_traffic(path=None, sources=None):
     if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_clock(path=None, sources=None):
+    """Sustained core clock and MFMA utilisation of the roofline kernel from
+    the committed counter run (GRBM_GUI_ACTIVE per XCD over the launch,
+    SQ_VALU_MFMA_BUSY_CYCLES per SIMD), with the fraction of the FP8 peak at
+    that clock; None when absent or taken on a different kernel source."""
+    try:
+        with open(path or CLOCK_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
+        return None
+    mhz = float(rec["clock_mhz"])
+    return {"mhz": mhz, "mfma_busy_of_active": rec["mfma_busy_of_active"], "launch_us": rec["launch_us"],
+            "tflops": rec["tflops"], "frac_at_clock": round(rec["tflops"] / (FP8_PEAK_TFLOPS * mhz / 2400.0), 4),
+            "source": rec.get("source")}
 
 
 def cpu_baseline(x_ffn, x_down, gate_blocks, down_blocks, gate, dn, m_rows=128):
@@ -799,6 +818,10 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
+            # the counter run's clock: its launch ran alone (counter
+            # collection serialises dispatches), so at a higher clock than
+            # the back-to-back timed pass
+            "clock": measured_clock(),
         },
         "phases_us": {k: round(v, 2) for k, v in ph.items()},
         "hbm_phases": hbm,
