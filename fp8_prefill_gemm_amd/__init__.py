@@ -142,6 +142,25 @@ def workspace(device, stream=None) -> "torch.Tensor":
     return _empty(lib().rz_workspace_bytes(), torch.uint8, device, stream)
 
 
+_ws_cache = {}
+
+
+def _call_workspace(device, stream=None):
+    """The workspace the calls below use when given none: one
+    rz_workspace_bytes() buffer per (device, stream), made on that stream.
+    Calls on one stream are ordered, so they can share it; calls on
+    different streams get their own."""
+    torch = _torch()
+    dev = torch.device(device)
+    st = _torch_stream(stream, dev)
+    key = (dev.index or 0, st.cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None:
+        buf = workspace(dev, st)
+        _ws_cache[key] = buf
+    return buf
+
+
 def rz_pad_m(m: int) -> int:
     return int(lib().rz_pad_m(m))
 
@@ -171,7 +190,7 @@ def rz_fp8_pack_weight(qtype: int, blocks, n: int, k: int, w_fp8=None, ws=None, 
     if w_fp8 is None:
         w_fp8 = _empty((n, k), torch.uint8, dev, stream)
     if ws is None:
-        ws = workspace(dev, stream)
+        ws = _call_workspace(dev, stream)
     scale = ctypes.c_float()
     amax = ctypes.c_float()
     _check(lib().rz_fp8_pack_weight(qtype, _ptr(blocks), n, k, _ptr(w_fp8), ctypes.addressof(scale),
@@ -193,7 +212,7 @@ def rz_fp8_pack_weights(weights, ws=None, stream=None):
         _require_cuda(b, w8)
         outs.append(_empty((n, k), torch.uint8, b.device, stream) if w8 is None else w8)
     if ws is None:
-        ws = workspace(dev, stream)
+        ws = _call_workspace(dev, stream)
     _require_cuda(ws)
     qt = (ctypes.c_int * cnt)(*[w[0] for w in weights])
     bp = (ctypes.c_void_p * cnt)(*[_ptr(w[1]) for w in weights])
@@ -219,7 +238,7 @@ def rz_fp8_quant_act(x, a_fp8=None, act_scale=None, ws=None, stream=None):
     if act_scale is None:
         act_scale = _empty(4, torch.float32, dev, stream)
     if ws is None:
-        ws = workspace(dev, stream)
+        ws = _call_workspace(dev, stream)
     _check(lib().rz_fp8_quant_act(_ptr(x), m, k, _ptr(a_fp8), _ptr(act_scale), _ptr(ws),
                                   _stream(stream, dev)))
     return a_fp8, act_scale
@@ -310,7 +329,7 @@ def rz_kquant_weight_scale(qtype: int, blocks, n: int, k: int, ws=None, stream=N
     _require_cuda(blocks, ws)
     dev = blocks.device
     if ws is None:
-        ws = workspace(dev, stream)
+        ws = _call_workspace(dev, stream)
     q, dq, amax = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
     _check(lib().rz_kquant_weight_scale(qtype, _ptr(blocks), n, k, ctypes.addressof(q), ctypes.addressof(dq),
                                         ctypes.addressof(amax), _ptr(ws), _stream(stream, dev)))

@@ -8,22 +8,23 @@
 //
 // The pages reduce with a shared-memory tree and a global atomic max into a
 // word that must first be zeroed by a host-to-device copy.  Here the
-// reduction is two-pass and atomic-free: pass 1 writes one key per
-// workgroup (wave shuffles + LDS), pass 2 (the encoder) starts by reducing
-// those keys in every workgroup, so no zeroing and no extra launch is
-// needed, and workgroup 0 publishes {absmax, absmax'/448} for the GEMM.
-// HBM traffic: read x twice (4 + 4 bytes per element) and write 1 byte.
+// reduction is atomic-free: pass 1 writes one key per workgroup (wave
+// shuffles + LDS), one workgroup reduces those keys and publishes
+// {absmax, absmax'/448} for the GEMM and the encode scale 448/absmax', and
+// pass 2 (the encoder) reads that record: no zeroing, nothing left over
+// between calls.  HBM traffic: read x twice (4 + 4 bytes per element) and
+// write 1 byte.
 #include <mutex>
 
 #include "rz_device.h"
 #include "rz_internal.h"
 
 // Scratch of rz_fp8_quant_act_noalloc: the partial absmax keys of one
-// activation quantisation (at most kMaxPartials of them).  One copy per GPU,
-// held until the process ends; host code reaches it only through the
-// address hipGetSymbolAddress returns for the current device
-// (quant_scratch_ptr), never through this name.
-static __device__ __align__(256) uint32_t scratch[rz::kMaxPartials];
+// activation quantisation (at most kMaxPartials of them), then the scale
+// record.  One copy per GPU, held until the process ends; host code reaches
+// it only through the address hipGetSymbolAddress returns for the current
+// device (quant_scratch_ptr), never through this name.
+static __device__ __align__(256) uint32_t scratch[rz::kQuantScratchBytes / 4];
 
 namespace rz {
 namespace {
@@ -68,20 +69,30 @@ __global__ __launch_bounds__(kThreads) void absmax_partial_kernel(const float* _
     if (threadIdx.x == 0) partial[blockIdx.x] = key;
 }
 
-// Pass 2 of the activation path.  count_real = m*k (a multiple of 256),
-// count_total = pad_m(m)*k; groups of 16 elements at or past count_real are
-// pad rows and are written as zero bytes.
-__global__ __launch_bounds__(kThreads) void act_encode_kernel(
-    const float* __restrict__ x, uint64_t count_real, uint64_t count_total,
-    const uint32_t* __restrict__ partial, int npartial, uint8_t* __restrict__ out,
-    float* __restrict__ act_scale) {
+// One workgroup: reduces the npartial keys and publishes {a, dq} to
+// act_scale and {a, q, dq, 0} to rec for the encode pass.
+__global__ __launch_bounds__(kThreads) void act_scales_kernel(const uint32_t* __restrict__ partial, int npartial,
+                                                              float* __restrict__ act_scale, float* __restrict__ rec) {
     __shared__ uint32_t red[kThreads / kWave];
     const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
+        rec[0] = sc.a;
+        rec[1] = sc.q;
+        rec[2] = sc.dq;
+        rec[3] = 0.0f;
         act_scale[0] = sc.a;
         act_scale[1] = sc.dq;
     }
-    const float q = sc.q;
+}
+
+// Pass 2 of the activation path.  count_real = m*k (a multiple of 256),
+// count_total = pad_m(m)*k; groups of 16 elements at or past count_real are
+// pad rows and are written as zero bytes.
+// rec: the {a, q, dq, 0} act_scales_kernel published.
+__global__ __launch_bounds__(kThreads) void act_encode_kernel(
+    const float* __restrict__ x, uint64_t count_real, uint64_t count_total,
+    const float* __restrict__ rec, uint8_t* __restrict__ out) {
+    const float q = rec[1];
     const uint64_t groups = count_total >> 4;
     const uint64_t real_groups = count_real >> 4;
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
@@ -183,13 +194,13 @@ int absmax_groups(uint64_t count) { return grid_for(((count >> 2) + kU - 1) / kU
 }  // namespace
 
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,
-                            uint8_t* a_fp8, float* act_scale, uint8_t* ws, hipStream_t st) {
-    uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
+                            uint8_t* a_fp8, float* act_scale, uint32_t* partial, uint8_t* tail, hipStream_t st) {
     const int g1 = absmax_groups(count_real);
+    float* rec = reinterpret_cast<float*>(tail);
     absmax_partial_kernel<<<g1, kThreads, 0, st>>>(x, count_real, partial);
+    act_scales_kernel<<<1, kThreads, 0, st>>>(partial, g1, act_scale, rec);
     const int g2 = grid_for(count_total >> 4, 4096);
-    act_encode_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, partial, g1, a_fp8,
-                                               act_scale);
+    if (count_total) act_encode_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, rec, a_fp8);
     return hipGetLastError();
 }
 

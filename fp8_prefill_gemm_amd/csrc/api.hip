@@ -340,8 +340,9 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8, flo
         ((uintptr_t)act_scale_dev & 3u))
         return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     if (int r = check_device(fn)) return r;
-    hipError_t e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8,
-                                        act_scale_dev, static_cast<uint8_t*>(ws), as_stream(stream));
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    hipError_t e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8, act_scale_dev,
+                                        reinterpret_cast<uint32_t*>(w), w + rz::kWsQuantOffset, as_stream(stream));
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }
 
@@ -354,17 +355,19 @@ int rz_fp8_quant_act_noalloc(const float* x, uint32_t m, uint32_t k, uint8_t* a_
     if (int r = check_k(fn, k)) return r;
     if ((uint64_t)rz_pad_m(m) * k > RZ_MAX_ELEMS || m > 0xFFFFFFF0u)
         return fail(RZ_ERR_SHAPE, "%s: m*k too large", fn);
+    // the partial keys, then the scale record at a fixed offset
     const uint64_t need = 4 * (uint64_t)rz::quant_act_partials((uint64_t)m * k);
-    if (need > RZ_QUANT_SCRATCH_BYTES)
-        return fail(RZ_ERR_SHAPE, "%s: %llu bytes of scratch needed, %u available", fn,
-                    (unsigned long long)need, (unsigned)RZ_QUANT_SCRATCH_BYTES);
+    if (need > 4 * (uint64_t)rz::kMaxPartials)
+        return fail(RZ_ERR_SHAPE, "%s: %llu bytes of partial keys needed, %u available", fn,
+                    (unsigned long long)need, (unsigned)(4 * rz::kMaxPartials));
     if ((m != 0 && (!aligned16(x) || !aligned16(a_fp8))) || ((uintptr_t)act_scale_dev & 3u))
         return fail(RZ_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     if (int r = check_device(fn)) return r;
     uint8_t* scratch = nullptr;
     hipError_t e = rz::quant_scratch_ptr(&scratch);
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8, act_scale_dev, scratch,
+    e = rz::launch_quant_act(x, (uint64_t)m * k, (uint64_t)rz_pad_m(m) * k, a_fp8, act_scale_dev,
+                             reinterpret_cast<uint32_t*>(scratch), scratch + 4 * (size_t)rz::kMaxPartials,
                              as_stream(stream));
     return e == hipSuccess ? RZ_OK : hip_fail(e, fn);
 }

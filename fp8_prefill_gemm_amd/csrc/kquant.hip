@@ -9,8 +9,9 @@
 // The pages stage the dequantised weight in an fp32 scratch tensor (write 4,
 // read 4, read 4 bytes per weight) before encoding.  Here the weight is
 // dequantised in registers twice instead: pass 1 reduces per-workgroup
-// absmax keys, pass 2 reduces those keys, derives the scales and re-decodes
-// the blocks straight into E4M3 bytes.  Traffic per weight: 2 x 0.5625 + 1
+// absmax keys, one workgroup per weight reduces those keys and publishes
+// the scales, and pass 2 re-decodes the blocks straight into E4M3 bytes
+// with them.  Traffic per weight: 2 x 0.5625 + 1
 // bytes (Q4_K), 2 x 0.8203 + 1 (Q6_K).  The decoded values are bit-identical
 // in both passes (integer unpacking and exact products).
 //
@@ -230,22 +231,17 @@ __global__ __launch_bounds__(kThreads) void pack_absmax_kernel(PackSet P, uint32
     if (threadIdx.x == 0) partial[blockIdx.x] = key;
 }
 
-// Pass 2 over a set of weights: weight i owns workgroups [g2[i], g2[i+1]).
-// Each workgroup reduces its weight's pass-1 keys, derives the scales and
-// encodes (a weight without an output, w_fp8[i] null, has one workgroup,
-// which only publishes the scales).  The first workgroup of weight i publishes {a, q, dq, 0} to
+// Workgroup i reduces weight i's pass-1 keys and publishes {a, q, dq, 0} to
 // scale_out[4i..] and, when host[i] is given, {a, q, dq} to that coherent
 // host memory followed by ticket[i] in its fourth word, stored with release
 // order at system scope: a host thread that sees the ticket there can read
-// the scales while the codes are still being written.
-template <int QT>
-__global__ __launch_bounds__(kThreads) void pack_encode_kernel(PackSet P, const uint32_t* __restrict__ partial,
+// the scales while pass 2 still writes the codes.
+__global__ __launch_bounds__(kThreads) void pack_scales_kernel(PackSet P, const uint32_t* __restrict__ partial,
                                                                float* __restrict__ scale_out) {
     __shared__ uint32_t red[kThreads / kWave];
-    const int i = set_member(P.g2, P.count, blockIdx.x);
-    const int bid = blockIdx.x - P.g2[i], ng = P.g2[i + 1] - P.g2[i];
+    const int i = blockIdx.x;
     const Scales sc = scales_from_key(reduce_partials<kThreads>(partial + P.g1[i], P.g1[i + 1] - P.g1[i], red));
-    if (bid == 0 && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
         float* so = scale_out + 4 * i;
         so[0] = sc.a;
         so[1] = sc.q;
@@ -259,13 +255,22 @@ __global__ __launch_bounds__(kThreads) void pack_encode_kernel(PackSet P, const 
                                __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
-    if (!P.w_fp8[i]) return;  // scales only (one workgroup)
-    const bool tensor_finite = sc.a <= 3.402823466e38f;
+}
+
+// Pass 2 over a set of weights: weight i owns workgroups [g2[i], g2[i+1])
+// (none when it has no output, w_fp8[i] null) and encodes with the q that
+// pack_scales_kernel published in scale_out[4i + 1].
+template <int QT>
+__global__ __launch_bounds__(kThreads) void pack_encode_kernel(PackSet P, const float* __restrict__ scale_out) {
+    const int i = set_member(P.g2, P.count, blockIdx.x);
+    const int bid = blockIdx.x - P.g2[i], ng = P.g2[i + 1] - P.g2[i];
+    const float a = scale_out[4 * i], q = scale_out[4 * i + 1];
+    const bool tensor_finite = a <= 3.402823466e38f;
     const int qt = QT ? QT : P.qtype[i];
     if (qt == 12)
-        encode_part<12>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], sc.q, tensor_finite);
+        encode_part<12>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], q, tensor_finite);
     else
-        encode_part<14>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], sc.q, tensor_finite);
+        encode_part<14>(P.blocks[i], P.nb[i], bid, ng, P.w_fp8[i], q, tensor_finite);
 }
 
 // Workgroups that give every thread `per` units of a Q4_K tensor (`per` / 2
@@ -321,24 +326,27 @@ hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* bl
         P.host[i] = host_scale ? host_scale[i] : nullptr;
         P.ticket[i] = ticket ? ticket[i] : 0u;
         P.g1[i + 1] = P.g1[i] + pack_absmax_groups(qtype[i], nb[i]);
-        // every encode workgroup re-reduces its weight's keys: keep their number bounded
-        P.g2[i + 1] = P.g2[i] + (w_fp8[i] ? clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials) : 1);
+        P.g2[i + 1] = P.g2[i] + (w_fp8[i] ? clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials) : 0);
         same = same && qtype[i] == qtype[0];
     }
     if (P.g1[count] > kWsPartials) return hipErrorInvalidValue;
     uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
     float* scale_out = reinterpret_cast<float*>(ws + kWsScaleOffset);
     const int g1 = P.g1[count], g2 = P.g2[count];
-    if (same && qtype[0] == 12) {
+    if (same && qtype[0] == 12)
         pack_absmax_kernel<12><<<g1, kThreads, 0, st>>>(P, partial);
-        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
-    } else if (same) {
+    else if (same)
         pack_absmax_kernel<14><<<g1, kThreads, 0, st>>>(P, partial);
-        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
-    } else {
+    else
         pack_absmax_kernel<0><<<g1, kThreads, 0, st>>>(P, partial);
-        pack_encode_kernel<0><<<g2, kThreads, 0, st>>>(P, partial, scale_out);
-    }
+    pack_scales_kernel<<<count, kThreads, 0, st>>>(P, partial, scale_out);
+    if (g2 == 0) return hipGetLastError();
+    if (same && qtype[0] == 12)
+        pack_encode_kernel<12><<<g2, kThreads, 0, st>>>(P, scale_out);
+    else if (same)
+        pack_encode_kernel<14><<<g2, kThreads, 0, st>>>(P, scale_out);
+    else
+        pack_encode_kernel<0><<<g2, kThreads, 0, st>>>(P, scale_out);
     return hipGetLastError();
 }
 

@@ -13,11 +13,15 @@ namespace rz {
 // Workspace layout (bytes): [0, 32768) partial absmax keys (uint32; one
 // reduction uses at most kMaxPartials of them, a pack set up to kWsPartials
 // in total), [32768, 33024) the weight path's {a, q, dq, 0}, one record per
-// weight of a pack set (room for 16).
+// weight of a pack set (room for 16), [33024, 33056) the activation
+// quantisation's record (kQuantTail: {a, q, dq, 0}).  Nothing in it needs
+// to start at zero: every call writes what it reads.
 constexpr int kMaxPartials = 2048;
 constexpr int kWsPartials = 8192;
 constexpr size_t kWsScaleOffset = 4 * (size_t)kWsPartials;
-constexpr size_t kWsBytes = kWsScaleOffset + 256;
+constexpr size_t kWsQuantOffset = kWsScaleOffset + 256;
+constexpr size_t kQuantTail = 32;  // float {a, q, dq, 0}, padded
+constexpr size_t kWsBytes = kWsQuantOffset + 256;
 
 // A set of weights packed by one pass-1 and one pass-2 launch (kquant.hip):
 // weight i owns pass-1 workgroups [g1[i], g1[i+1]) (and their partial keys,
@@ -39,10 +43,11 @@ struct PackSet {
 // ---- kquant.hip
 hipError_t launch_dequant_f32(int qtype, const uint8_t* blocks, uint64_t nblocks, float* out,
                               hipStream_t st);
-// Two kernels: partial absmax keys, then (reduce + encode).  Writes
-// {a, q, dq, 0} as floats at ws + kWsScaleOffset and, when host_scale is not
-// null, {a, q, dq} to that coherent host memory followed by `ticket` (as a
-// uint32, release order) in its fourth word, before the codes.
+// Three kernels: partial absmax keys, one workgroup per weight that
+// reduces them and publishes the scales, then the encode.  Writes
+// {a, q, dq, 0} as floats at ws + kWsScaleOffset and, when host_scale is
+// not null, {a, q, dq} to that coherent host memory followed by `ticket`
+// (as a uint32, release order) in its fourth word, before the codes.
 hipError_t launch_pack(int qtype, const uint8_t* blocks, uint64_t nblocks, uint8_t* w_fp8,
                        uint8_t* ws, float* host_scale, uint32_t ticket, hipStream_t st);
 // w_fp8 may be null: then only the scales are computed and published (the
@@ -69,13 +74,17 @@ hipError_t launch_kquant_fp8_gemm(const uint8_t* a_fp8, uint32_t m, const float*
                                   hipStream_t st);
 
 // ---- actquant.hip
+// Three kernels: partial absmax keys, one workgroup that reduces them and
+// publishes {a, dq} to act_scale and {a, q, dq, 0} to tail, then the
+// encode.  partial: kMaxPartials uint32; tail: kQuantTail bytes.
 hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_total,
-                            uint8_t* a_fp8, float* act_scale, uint8_t* ws, hipStream_t st);
+                            uint8_t* a_fp8, float* act_scale, uint32_t* partial, uint8_t* tail, hipStream_t st);
 // Partial keys launch_quant_act writes for count_real elements (<= kMaxPartials).
 int quant_act_partials(uint64_t count_real);
 // Device address of the quantisation scratch array (kQuantScratchBytes) of
-// the current device, looked up once per device.
-constexpr size_t kQuantScratchBytes = 4 * (size_t)kMaxPartials;
+// the current device, looked up once per device: the partial keys, then the
+// scale record.
+constexpr size_t kQuantScratchBytes = 4 * (size_t)kMaxPartials + kQuantTail;
 hipError_t quant_scratch_ptr(uint8_t** ptr);
 // fp16 copy of x (count_real values, then zeros up to count_total).
 hipError_t launch_fp16_convert(const float* x, uint64_t count_real, uint64_t count_total, uint16_t* out,

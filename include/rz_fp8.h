@@ -29,7 +29,8 @@
  *   - K (the reduction dimension) must be a positive multiple of 256, the
  *     K-quant super-block length (RZ_ERR_SHAPE otherwise).
  *   - `ws` is a caller-provided device workspace of rz_workspace_bytes()
- *     bytes.  Calls that use the same `ws` must be ordered (same stream).
+ *     bytes (any contents: every call writes what it reads).  Calls that
+ *     use the same `ws` must be ordered (same stream).
  */
 #ifndef RZ_FP8_H
 #define RZ_FP8_H
@@ -142,8 +143,8 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
                      float* act_scale_dev, void* ws, void* stream);
 
 /* Bytes of the device scratch array rz_fp8_quant_act_noalloc uses on each
- * GPU (2048 partial absmax keys). */
-#define RZ_QUANT_SCRATCH_BYTES 8192u
+ * GPU (2048 partial absmax keys and the scale record). */
+#define RZ_QUANT_SCRATCH_BYTES 8224u
 
 /*
  * rz_fp8_quant_act without a workspace argument and without any allocation,
@@ -151,14 +152,15 @@ int rz_fp8_quant_act(const float* x, uint32_t m, uint32_t k, uint8_t* a_fp8,
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, results and error behaviour as rz_fp8_quant_act, minus `ws`.
  *
- * Its scratch (the partial absmax keys) is a fixed array of
+ * Its scratch (the partial absmax keys and the scale record) is a fixed
+ * array of
  * RZ_QUANT_SCRATCH_BYTES in the library's device image, one copy per GPU,
  * held until the process ends; its address is looked up on the first call
  * on each device.  A quantisation needs at most 2048 keys whatever m*k
  * (the reduction caps its grid), so every size accepted by rz_fp8_quant_act
  * fits; a size that would need more is rejected with RZ_ERR_SHAPE.  Nothing
- * in the scratch needs to start at zero: every call writes the keys it
- * reads.  All calls on one GPU share the array, so calls that overlap in
+ * in the scratch needs to start at zero: every call writes the keys and the
+ * record it reads.  All calls on one GPU share the array, so calls that overlap in
  * time on one GPU (different streams, or other host threads) race and must
  * be ordered by the caller; calls on one stream are ordered by the stream.
  * Calls no hipMalloc, hipFree or allocating library routine.

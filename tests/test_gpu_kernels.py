@@ -209,6 +209,29 @@ def test_pack_reuses_workspace(rz):
         np.testing.assert_array_equal(host(w8), r8)
 
 
+def test_quant_and_pack_share_a_workspace_in_turn(rz):
+    # The last workgroup of each pass-1 launch reduces the keys and returns
+    # the arrival counter to zero: calls of different sizes (1 and 2048 pass-1
+    # workgroups, a pack set of 3 weights) alternate on one workspace and
+    # each still elects its last arrival and matches the oracle bit for bit.
+    ws = rz.workspace("cuda")
+    g = np.random.Generator(np.random.PCG64(41))
+    for m, k in [(1, 256), (2048, 3584), (3, 512), (2048, 3584), (1, 256)]:
+        x = W.act_student_t(int(g.integers(1 << 30)), m, k)
+        a8, sc = rz.rz_fp8_quant_act(dev(x), ws=ws)
+        r8, ra, rdq = fp8_path.quant_act(x)
+        sc = host(sc)
+        assert sc[0].view(np.uint32) == ra.view(np.uint32) and sc[1].view(np.uint32) == rdq.view(np.uint32)
+        np.testing.assert_array_equal(host(a8), r8)
+        packs = [(W.Q4_K, W.q4k_blocks(m + 1, 64, 512), 64, 512), (W.Q6_K, W.q6k_blocks(m + 2, 32, 768), 32, 768),
+                 (W.Q4_K, W.q4k_blocks(m + 3, 300, 256), 300, 256)]
+        outs = rz.rz_fp8_pack_weights([(qt, dev(b), n, kk, None) for qt, b, n, kk in packs], ws=ws)
+        for (qt, b, n, kk), (w8, scale, amax) in zip(packs, outs):
+            r8w, rdqw, raw = fp8_path.pack_weight(qt, b, n, kk)
+            assert np.float32(scale) == rdqw and np.float32(amax) == raw
+            np.testing.assert_array_equal(host(w8), r8w)
+
+
 # ------------------------------------------------------------------ activation
 
 @pytest.mark.parametrize("m,k,kind", [(16, 512, "normal"), (1, 3584, "student_t"),
