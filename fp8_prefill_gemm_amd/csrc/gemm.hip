@@ -469,11 +469,11 @@ GemmPlan plan_gemm(uint32_t m, uint32_t n, uint32_t k, int cus, bool split_allow
     } else if (p.kind != kGemmTiles) {
         const int T = ceil_div(mp, p.bm) * ceil_div((int)n, p.bn);
         p.workgroups = T;
-        p.s = split_allowed ? edge_split(p.kind, mp, n, k) : 1;
+        p.s = split_allowed && T <= kSplitMaxTiles ? edge_split(p.kind, mp, n, k) : 1;
         if (p.s > 1) {  // XCD x runs the chunks of its own tiles (tile_of_workgroup)
             p.rem = T;
             p.workgroups = kXcds * ceil_div(T, kXcds) * p.s;
-            p.ws_bytes = split_counter_bytes(T) + (size_t)T * p.s * p.bn * p.bm * sizeof(float);
+            p.ws_bytes = kSplitCounterBytes + (size_t)T * p.s * p.bn * p.bm * sizeof(float);
         }
     }
     return p;

@@ -37,6 +37,14 @@ __device__ __forceinline__ v16f mma32(const v8i& src0, const v8i& src1, v16f acc
     }
 }
 
+// Cache-policy operand of the raw buffer load/store builtins on gfx950: its
+// bits 0 and 4 are the instruction's SC0 and SC1 scope bits.  Device scope
+// (SC1): a store writes through the XCD's L2 and completes once it is
+// visible to every XCD.  System scope (SC0 and SC1): a load misses in the
+// L1 and the L2 and reads memory.
+constexpr int kScopeDevice = 16;
+constexpr int kScopeSystem = 17;
+
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
 

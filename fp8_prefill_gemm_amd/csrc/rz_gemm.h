@@ -52,8 +52,13 @@ hipError_t launch_fp16_gemm(const uint16_t* a_f16, const uint16_t* w_f16, uint32
 // bytes; kinds kGemmLargeEdge, kGemmMedium, kGemmSmall; no split).
 hipError_t launch_gemm_edge_fp16(const GemmPlan& p, const uint8_t* a, const uint8_t* w, uint32_t m, uint32_t n,
                                  uint32_t kb, float* y, hipStream_t st);
-// Split-K workspace: arrival counters of the split tiles (one uint32 each),
-// padded to 256 bytes; the partial sums follow.
-inline size_t split_counter_bytes(int tiles) { return ((size_t)tiles * sizeof(unsigned) + 255) / 256 * 256; }
+// Split-K workspace: one arrival counter (uint32) per tile in a region of
+// fixed size at its start, the partial sums after it.  The region does not
+// depend on the shape, so a workspace shared by calls of different shapes
+// never finds one call's partial sums where the next keeps its counters
+// (every call leaves its counters at zero; the partial sums are written
+// before they are read).  Only plans with at most kSplitMaxTiles tiles split.
+constexpr int kSplitMaxTiles = 256;
+constexpr size_t kSplitCounterBytes = kSplitMaxTiles * sizeof(unsigned);
 
 }  // namespace rz

@@ -182,7 +182,8 @@ int rz_fp8_quant_act_noalloc(const float* x, uint32_t m, uint32_t k, uint8_t* a_
  *   y             device out, fp32 [m][n] row-major (only rows < m written)
  *   ws, ws_bytes  optional device workspace (may be NULL / 0) of at least
  *                 rz_fp8_gemm_workspace_bytes(m, n, k) bytes, zero-filled
- *                 before its first use; every call leaves it reusable.  It
+ *                 before its first use; every call leaves it reusable by
+ *                 the next, whatever that call's shape.  It
  *                 holds partial sums and arrival counters when a shape with
  *                 few output tiles (small or medium m, narrow n) splits K
  *                 to keep the compute units busy; without it (or when it is

@@ -235,15 +235,15 @@ def test_gemm_group_validation(L):
 
 def test_gemm_workspace_sizes(L):
     # the GEMV and skinny kernels (padded M <= 64) need none; split-K with 64x32 tiles:
-    # 256 bytes of arrival counters + 12 tiles x 2 chunks of 64x32 fp32
+    # 1 KB of arrival counters (256, whatever the shape) + 12 tiles x 2 chunks of 64x32 fp32
     assert L.rz_fp8_gemm_workspace_bytes(16, 256, 512) == 0
-    assert L.rz_fp8_gemm_workspace_bytes(80, 256, 512) == 256 + 12 * 2 * 64 * 32 * 4
+    assert L.rz_fp8_gemm_workspace_bytes(80, 256, 512) == 1024 + 12 * 2 * 64 * 32 * 4
     assert L.rz_fp8_gemm_workspace_bytes(0, 256, 512) == 0
     assert L.rz_fp8_gemm_workspace_bytes(2048, 256, 300) == 0
     # interior-tile plans need none; the 128x128 split needs counters + 2 chunks of 112 tiles
     assert L.rz_fp8_gemm_workspace_bytes(2048, 18944, 3584) == 0
     assert L.rz_fp8_gemm_workspace_bytes(2048, 3584, 18944) == 0
-    assert L.rz_fp8_gemm_workspace_bytes(512, 3584, 3584) == 512 + 112 * 2 * 128 * 128 * 4
+    assert L.rz_fp8_gemm_workspace_bytes(512, 3584, 3584) == 1024 + 112 * 2 * 128 * 128 * 4
 
 
 def test_diagnostics_validation(L):
@@ -288,7 +288,9 @@ def _edge_plan(m, n, k, cus=256):
     the skinny kernel (16 weight rows per workgroup) when M_pad <= 64; 256x256 tiles from 256 tiles on, unsplit; else 128x128 tiles
     split into s = min(256 // tiles, pairs // 2) K chunks if M_pad >= 128 and
     that gives >= 128 workgroups; else 64x32 tiles in s = min(512 // tiles,
-    pairs) chunks.  A split rounds the tiles up to a multiple of 8 (XCDs)."""
+    pairs) chunks.  A split rounds the tiles up to a multiple of 8 (XCDs);
+    its workspace is a fixed 1 KB of arrival counters (up to 256 tiles) and
+    the partial sums."""
     mp = -(-m // 16) * 16
     pairs = k // 256
     if m <= 3:
@@ -311,7 +313,7 @@ def _edge_plan(m, n, k, cus=256):
         s = max(1, min(512 // t, pairs))
     if s == 1:
         return bn, bm, t, 0
-    return bn, bm, 8 * -(-t // 8) * s, -(-4 * t // 256) * 256 + t * s * bn * bm * 4
+    return bn, bm, 8 * -(-t // 8) * s, 1024 + t * s * bn * bm * 4  # 256 counters, then the partials
 
 
 def _interior_items(T, W):

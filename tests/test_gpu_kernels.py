@@ -487,6 +487,34 @@ def test_gemm_edge_split_plans(rz, m, n, k, full):
     assert (host(ws[:4 * tiles]) == 0).all()  # arrival counters left at zero for the next call
 
 
+def test_gemm_split_shapes_share_one_workspace(rz):
+    # split-K shapes of different tile counts in turn on one workspace: the
+    # counters sit in a region of fixed size, so one shape's partial sums
+    # never land where the next shape keeps its counters
+    shapes = [(2048, 512, 3584),   # 128x128 tiles: 64 tiles in 4 chunks
+              (512, 3584, 3584),   # 112 tiles in 2 chunks
+              (512, 512, 3584),    # 64x32 tiles: 128 tiles in 4 chunks
+              (80, 200, 768),      # 64x32 tiles: 12 tiles in 3 chunks
+              (2048, 512, 3584)]
+    need = max(rz.rz_fp8_gemm_workspace_bytes(m, n, k) for m, n, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (m, n, k) in enumerate(shapes):
+        assert rz.rz_fp8_gemm_workspace_bytes(m, n, k) > 0
+        g = np.random.Generator(np.random.PCG64(31 * i + m + n))
+        mp = fp8_path.pad_m(m)
+        a8 = _codes(g, (mp, k))
+        a8[m:] = 0
+        w8 = _codes(g, (n, k))
+        sc = np.array([1.0, 0.018, 0, 0], np.float32)
+        wdq = np.float32(0.0077)
+        rows = np.unique(np.concatenate([[0, m - 1], g.choice(m, min(m, 40), replace=False)]))
+        yr, tol = fp8_path.gemm_rows(a8, w8, rows, sc[1], wdq)
+        y = host(rz.rz_fp8_gemm(dev(a8), dev(w8), m, dev(sc), float(wdq), ws=ws))
+        err = np.abs(y[rows].astype(np.float64) - yr)
+        assert (err <= tol).all(), f"shape {(m, n, k)}: {(err > tol).sum()} out of bound"
+        assert (host(ws[:1024]) == 0).all()  # every counter back at zero
+
+
 def test_gemm_split_on_two_streams(rz):
     # split-K GEMMs issued alternately on two streams through the binding's
     # default workspace: each stream gets its own zero-filled workspace, so
