@@ -49,6 +49,7 @@ path's GEMM, at the model's prefill shapes (warm).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -615,8 +616,11 @@ def q8_gemm(args, dev) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the defaults time the clocks' steady state: after only a few warm-up
+    # steps the GPU is still raising its clock (measured: gate+up launch 0.38
+    # of peak after 3 warm-up steps, 0.43 after 10, 0.45-0.46 from 100 on)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -750,12 +754,18 @@ def main() -> int:
     # timed pass: only the markers around the gate and up GEMMs
     gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
+    # no garbage collection inside the timed loop: a full collection over the
+    # interpreter's objects stalls the host for milliseconds, and the host
+    # issues every launch of the next phase after the pack's scale readback
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(gemm_events=gev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev])) * 1e3
 
     # diagnostic pass (not timed as a whole): markers between every phase
