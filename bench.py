@@ -45,6 +45,13 @@ accuracy on the gate GEMM.
 --kquant-gemm instead times the FP8 GEMM that encodes the weight from its
 K-quant blocks inside the kernel (no FP8 weight cache) beside the cached
 path's GEMM, at the model's prefill shapes (warm).
+
+--hbm-rates instead times torch's own device kernels on 1 GiB (a max and a
+sum that only read, a copy, a fill that only writes), cold (after a 1 GiB
+write) and warm, and a 155 MB max right after a 310 MB write (the down
+input's absmax after the gate+up GEMM's output): the rates plain kernels
+reach on this GPU, beside the 8 TB/s peak the HBM-bound phases are priced
+against.
 """
 from __future__ import annotations
 
@@ -219,6 +226,57 @@ def pack_model(args, dev) -> int:
            "data": "synthetic", "config": {"workload": "28 layers x {q,k,v,o,gate,up,down} at hidden 3584, "
                                                     "kv 512, FFN 18944; v and down Q6_K, the rest Q4_K"}}
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def hbm_rates(args, dev) -> int:
+    """Rates of torch's own read, copy and write kernels (one line; median of
+    9 runs each, HIP events around one launch)."""
+    import torch
+
+    n = 1 << 28  # 1 GiB of fp32
+    x = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+    y = torch.empty_like(x)
+    evict = torch.empty_like(x)
+
+    def timed(fn, cold, before=None):
+        ts = []
+        for _ in range(9):
+            if cold:
+                evict.fill_(1.0)  # 1 GiB written: the L2s and the 256 MB MALL hold none of x
+            if before is not None:
+                before()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    for _ in range(20):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    gib = n * 4
+    rows = {}
+    for name, fn, byts in (("amax (read)", lambda: torch.amax(x), gib), ("sum (read)", lambda: x.sum(), gib),
+                           ("copy (read + write)", lambda: y.copy_(x), 2 * gib),
+                           ("fill (write)", lambda: y.fill_(2.0), gib)):
+        for cold in (True, False):
+            t = timed(fn, cold)
+            rows[f"{name}, {'cold' if cold else 'warm'}"] = {"us": round(t * 1e6, 1),
+                                                           "tb_per_s": round(byts / t / 1e12, 2)}
+    a = x[:2048 * 18944]
+    out = y[:2048 * 37888]
+    t = timed(lambda: torch.amax(a), False, before=lambda: out.fill_(3.0))
+    rows["amax of 155 MB after a 310 MB write"] = {"us": round(t * 1e6, 1),
+                                                   "tb_per_s": round(a.numel() * 4 / t / 1e12, 2)}
+    for k, v in rows.items():
+        log(f"{k}: {v}")
+    print(json.dumps({"metric": "HBM rates of plain device kernels (torch), 1 GiB", "unit": "TB/s",
+                      "higher_is_better": True, "peak_tb_per_s": HBM_PEAK_TBPS, "rows": rows,
+                      "data": "synthetic", "config": {"workload": "1 GiB fp32 tensors; 155 MB / 310 MB FFN sizes"}}),
+          flush=True)
     return 0
 
 
@@ -636,6 +694,8 @@ def main() -> int:
                     help="instead time the FP16 cached-weight comparator beside the FP8 path (warm, M=2048 FFN)")
     ap.add_argument("--q8-gemm", action="store_true",
                     help="instead time the integer path (Q8_1 activation x Q4_K weight) beside the FP8 path (warm)")
+    ap.add_argument("--hbm-rates", action="store_true",
+                    help="time torch's read, copy and write kernels on 1 GiB instead (HBM rates on this GPU)")
     ap.add_argument("--kquant-gemm", action="store_true",
                     help="instead time the GEMM straight from K-quant blocks beside the cached path (warm)")
     args = ap.parse_args()
@@ -666,6 +726,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB read + 1 GiB write done")
         del src, dst
+    if args.hbm_rates:
+        return hbm_rates(args, dev)
     if args.pack_model:
         return pack_model(args, dev)
     if args.gemm_shapes:
