@@ -356,8 +356,8 @@ def test_interior_plan_examples(L):
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(8, 74), (8, 148), (8, 14), (16, 14), (16, 148), (3, 100), (2, 74),
                                              (1, 64), (8, 32), (5, 13)])
-def test_interior_schedule_covers_tiles_once(tiles_m, tiles_n):
-    W = 32
+@pytest.mark.parametrize("W", [32, 2, 3, 31, 38])  # workgroups per XCD: CUs / 8 (32 on MI355X; odd when harvested)
+def test_interior_schedule_covers_tiles_once(tiles_m, tiles_n, W):
     T = tiles_m * tiles_n
     items = _interior_items(T, W)
     seen = {}
