@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <chrono>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -123,7 +124,7 @@ const char* rz_last_error_string(void) { return g_last_error.c_str(); }
 const char* rz_version(void) { return "rz_fp8 0.1.0 gfx950"; }
 
 // Per-thread slot of fine-grained (coherent) pinned host memory that the
-// pack's encode kernel writes the scales into, followed by the call's ticket
+// pack's scale kernel writes the scales into, followed by the call's ticket
 // (below), so the host scale needs neither a device-to-host copy nor a
 // stream synchronisation.  Allocated on first use, kept until the process
 // ends; null if the allocation fails (then the scales are copied back and
@@ -145,18 +146,26 @@ static float* host_scale_slot() {
     return slot;
 }
 
-// Waits until `ticket` appears at *tag (written by the pack's encode kernel
-// with release order once the scales are in the slot).  The stream is
-// queried every 256 polls, so a stream that finishes, or fails, without
-// publishing the ticket ends the wait with an error instead of a hang.
+// Waits until `ticket` appears at *tag (written by the pack's scale kernel
+// with release order once the scales are in the slot).  After the first
+// millisecond the stream is queried once a millisecond, so a stream that
+// finishes, or fails, without publishing the ticket ends the wait with an
+// error instead of a hang.  Not sooner: each query costs the GPU a few
+// microseconds between the kernels queued around it (measured: the gap
+// between the pack and the next launch fell from 5.7 to 0 us when the
+// query every 256 polls went).
 static hipError_t wait_for_ticket(const uint32_t* tag, uint32_t ticket, hipStream_t st) {
+    using clock = std::chrono::steady_clock;
+    const clock::time_point t0 = clock::now();
+    clock::time_point next_query = t0 + std::chrono::milliseconds(1);
     for (uint32_t i = 1;; ++i) {
         if (__atomic_load_n(tag, __ATOMIC_ACQUIRE) == ticket) return hipSuccess;
-        if ((i & 255u) == 0) {
+        if ((i & 4095u) == 0 && clock::now() >= next_query) {
             const hipError_t q = hipStreamQuery(st);
             if (q == hipSuccess)
                 return __atomic_load_n(tag, __ATOMIC_ACQUIRE) == ticket ? hipSuccess : hipErrorUnknown;
             if (q != hipErrorNotReady) return q;
+            next_query = clock::now() + std::chrono::milliseconds(1);
         }
         __builtin_ia32_pause();
     }
