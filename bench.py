@@ -14,8 +14,9 @@ HBM before timing.
 value = GEMM FLOPs of the step (3 x 2*M*N*K) / measured step time, TFLOP/s.
 roofline = the gate+up GEMM launch (one rz_fp8_gemm_group call, 2 x 2*M*N*K
 per launch) timed with HIP events on its stream during the timed steps (the
-only markers in the timed loop), against the 5.0 PFLOP/s dense FP8 peak.  phases_us comes from a
-second, untimed pass of the same steps with markers between all phases.
+only markers in the timed loop, around that launch on every 4th step),
+against the 5.0 PFLOP/s dense FP8 peak.  phases_us comes from a second,
+untimed pass of the same steps with markers between all phases.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload (see
 --help).
 
@@ -813,8 +814,11 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed pass: only the markers around the gate and up GEMMs
-    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timed pass: the only markers are the two around the gate+up GEMM
+    # launch, on every 4th step (each marker leaves a 3-6 us gap between
+    # kernels, so markers on every step would add ~9 us to each)
+    every = 4
+    gev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, args.steps, every)}
     log(f"timing {args.steps} steps")
     # no garbage collection inside the timed loop: a full collection over the
     # interpreter's objects stalls the host for milliseconds, and the host
@@ -824,11 +828,11 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(gemm_events=gev[i])
+        step(gemm_events=gev.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
-    gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev])) * 1e3
+    gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev.values()])) * 1e3
 
     # diagnostic pass (not timed as a whole): markers between every phase
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
