@@ -326,7 +326,10 @@ hipError_t launch_pack_set(int count, const int* qtype, const uint8_t* const* bl
         P.host[i] = host_scale ? host_scale[i] : nullptr;
         P.ticket[i] = ticket ? ticket[i] : 0u;
         P.g1[i + 1] = P.g1[i] + pack_absmax_groups(qtype[i], nb[i]);
-        P.g2[i + 1] = P.g2[i] + (w_fp8[i] ? clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), kMaxPartials) : 0);
+        // pass 2 writes no keys: its grid is not capped at kMaxPartials (an
+        // 18944 x 3584 weight takes 4144 workgroups; capped at 2048 the
+        // step's pass 2 took 8 us longer)
+        P.g2[i + 1] = P.g2[i] + (w_fp8[i] ? clamp_groups(groups_for(qtype[i], nb[i], kEncodeUnits), 1 << 16) : 0);
         same = same && qtype[i] == qtype[0];
     }
     if (P.g1[count] > kWsPartials) return hipErrorInvalidValue;
