@@ -139,14 +139,25 @@ __device__ __forceinline__ Scales scales_from_key(uint32_t key) {
 }
 
 // Reduce `count` partial keys (written by an earlier kernel on the same
-// stream) to one key; every thread gets it.  Contains barriers.
+// stream) to one key; every thread gets it.  Contains barriers.  Each
+// thread issues the loads of up to 8 keys before it compares any, so the
+// common case (count <= 8 * kThreads) waits for one round trip instead of
+// one per key (a single workgroup runs this: measured 4.6 us per call with
+// the loads one after another).
 template <int kThreads>
 __device__ __forceinline__ uint32_t reduce_partials(const uint32_t* __restrict__ part, int count,
                                                     uint32_t* smem) {
+    constexpr int kPer = 8;
     uint32_t v = 0;
-    for (int i = threadIdx.x; i < count; i += kThreads) {
-        const uint32_t p = part[i];
-        v = v > p ? v : p;
+    for (int i0 = threadIdx.x; i0 < count; i0 += kPer * kThreads) {
+        uint32_t p[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = i0 + u * kThreads;
+            p[u] = i < count ? part[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) v = v > p[u] ? v : p[u];
     }
     return block_max_u32<kThreads>(v, smem);
 }
