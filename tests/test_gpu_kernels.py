@@ -209,11 +209,31 @@ def test_pack_reuses_workspace(rz):
         np.testing.assert_array_equal(host(w8), r8)
 
 
+def test_pack_waits_behind_a_busy_stream(rz):
+    # the pack's host wait polls for its scales and, after the first
+    # millisecond, also queries the stream once a millisecond: a pack queued
+    # behind ~20 ms of other work on a side stream still returns its scales
+    # (and codes) bit-exact
+    blocks = W.weight_blocks(W.Q4_K, 1700, 512, 3584)
+    b = dev(blocks)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print("pack behind a 20 ms spin on a side stream", flush=True)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(int(40e6))  # ~40M cycles: well over 1 ms at any clock
+        w8, scale, amax = rz.rz_fp8_pack_weight(W.Q4_K, b, 512, 3584, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    r8, rdq, ra = fp8_path.pack_weight(W.Q4_K, blocks, 512, 3584)
+    assert np.float32(amax).view(np.uint32) == ra.view(np.uint32)
+    assert np.float32(scale).view(np.uint32) == rdq.view(np.uint32)
+    np.testing.assert_array_equal(host(w8), r8)
+
+
 def test_quant_and_pack_share_a_workspace_in_turn(rz):
-    # The last workgroup of each pass-1 launch reduces the keys and returns
-    # the arrival counter to zero: calls of different sizes (1 and 2048 pass-1
-    # workgroups, a pack set of 3 weights) alternate on one workspace and
-    # each still elects its last arrival and matches the oracle bit for bit.
+    # Quantisations and packs of different sizes (1 and 2048 pass-1
+    # workgroups, a pack set of 3 weights) alternate on one workspace: each
+    # writes the partial keys and scale records it reads, so none sees
+    # another's leftovers, and every result matches the oracle bit for bit.
     ws = rz.workspace("cuda")
     g = np.random.Generator(np.random.PCG64(41))
     for m, k in [(1, 256), (2048, 3584), (3, 512), (2048, 3584), (1, 256)]:
