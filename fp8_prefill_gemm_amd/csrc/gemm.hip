@@ -77,7 +77,8 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* base, uint32_t lo, uint32_
 
 // One 128-byte K-step for one wave of a 256 x (64*TM) tile: 2x2 waves of
 // 128 x 32*TM, i.e. 4 x TM MFMA tiles of 32x32, two 64-byte K halves
-// (TM = 4: whole 256x256 tile; TM = 2: half tile of 128 activation rows).
+// (TM = 4: whole 256x256 tile; TM = 2: half tile of 128 activation rows;
+// TM = 1: quarter tile of 64).
 //   cur  LDS slot holding this step's operands (256 weight rows, then the
 //        activation rows, 128 bytes each);
 //   nxt  the other slot, which receives the next step's operands;
@@ -90,14 +91,16 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* base, uint32_t lo, uint32_
 // the program order is exactly: fragment reads for the next group, 4 MFMAs
 // with the group's chunk writes and loads between them (2 of each for
 // TM = 4, 3 for TM = 2).  A chunk load therefore has two full steps to land
-// before the same group of the step after next writes it to LDS.  The
-// caller places a workgroup barrier after each step.
+// before the same group of the step after next writes it to LDS.  (A
+// quarter tile has two groups of 4 MFMAs, each with 5 chunk writes and
+// loads; its first group also reads all of the second K half's weight
+// fragments.)  The caller places a workgroup barrier after each step.
 template <int TM, bool F16>
 __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, uint8_t* nxt,
                                       u32x4 (&x)[8 + 2 * TM], __amdgpu_buffer_rsrc_t wrs,
                                       __amdgpu_buffer_rsrc_t ars, uint32_t voff, uint32_t kb, uint32_t step,
                                       const PipeOffsets& o) {
-    static_assert(TM == 4 || TM == 2, "whole or half tile");
+    static_assert(TM == 4 || TM == 2 || TM == 1, "whole, half or quarter tile");
     constexpr int kRow32 = 32 * kBK;  // 32 rows
     constexpr int kGroups = 2 * TM;
     constexpr int kPer = (8 + 2 * TM) / kGroups;  // chunks per group
@@ -117,7 +120,12 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
             const int gn = g + 1;
             b[gn & 1] = frag_at(cur + (gn % TM) * kRow32, o.fb[gn / TM][0], o.fb[gn / TM][1]);
         }
-        if (g == kA1 || g == kA1 + 1) {  // two weight fragments per group
+        if constexpr (TM == 1) {  // one group per K half: all four now
+            if (g == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[1][i] = frag_at(cur + i * kRow32, o.fa[1][0], o.fa[1][1]);
+            }
+        } else if (g == kA1 || g == kA1 + 1) {  // two weight fragments per group
 #pragma unroll
             for (int i = 2 * (g - kA1); i < 2 * (g - kA1) + 2; ++i)
                 a[1][i] = frag_at(cur + i * kRow32, o.fa[1][0], o.fa[1][1]);
@@ -148,6 +156,24 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][TM], const uint8_t* cur, ui
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        } else if constexpr (TM == 1) {
+            if (g == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 20, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            }
+#pragma unroll
+            for (int mm = 0; mm < 3; ++mm) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
+                if (mm < 2) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
         } else {
             if (g == 0)
@@ -272,11 +298,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
 //   R = Tx / W whole rounds: tile r*W + j of the run in round r;
 //   the L = Tx - R*W tiles left over run as half tiles of 128 activation
 //   rows when a whole round comes before them or their 2L halves fit one
-//   round (else as whole tiles, one each for workgroups j < L).
-// Half tiles go out in half_rank order (the odd workgroups first), and an
-// odd workgroup runs its first half tile before its whole tiles, an even
-// one after them: the two halves of an XCD then reach the end of their
-// whole tiles half a tile apart.  Measured on the 256x256 tiles, the 256 KB
+//   round (else as whole tiles, one each for workgroups j < L).  When the
+//   2L halves are more than W but at most 1.5 W, every workgroup takes one
+//   half and the halves beyond the first W run as quarter tiles of 64
+//   activation rows instead, at most one per workgroup, so that no
+//   workgroup runs two halves (a half tile costs ~0.6 of a whole one).
+// Half and quarter tiles go out in half_rank order (the odd workgroups
+// first), and an odd workgroup runs its first half tile before its whole
+// tiles, an even one after them: the two halves of an XCD then reach the
+// end of their whole tiles half a tile apart.  Measured on the 256x256 tiles, the 256 KB
 // output store of a tile takes ~7k cycles when 16 CUs of an XCD store
 // together and ~16k when all 32 do, whether or not the other XCDs store at
 // the same time (the XCD's write path is the limit, not HBM).
@@ -329,20 +359,26 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
     const int Tx = tall + (x < trem ? 1 : 0);
     const int R = Tx / P.W, L = Tx - R * P.W;
     const bool halves = R > 0 || 2 * L <= P.W;
-    const int H = halves ? 2 * L : 0;  // half tiles of this XCD
+    int H = halves ? 2 * L : 0;  // half tiles of this XCD
+    int Q = 0;                   // quarter tiles: halves H.. of the left-over tiles, split
+    if (H > P.W && 2 * (H - P.W) <= P.W) {
+        Q = 2 * (H - P.W);
+        H = P.W;
+    }
     const int hr = half_rank(j, P.W);
     // items in order: [half hr if j is odd] [whole rounds] [the left-over
-    // whole tile j] [halves hr (j even), hr + W, hr + 2W, ...]
+    // whole tile j] [halves hr (j even), hr + W, hr + 2W, ...] [quarter hr]
     const bool early = (j & 1) && hr < H;
     int idx = early ? -1 : 0;  // -1: the early half; 0..R-1: rounds; R: left-over whole tile
     int hnext = early ? hr + P.W : hr;
+    bool quarter_left = hr < Q;
     for (;;) {
-        bool half = false;
-        int lt, mh = 0;  // tile of the XCD's run, activation half
+        int part = 4;    // activation rows / 64: 4 whole, 2 half, 1 quarter
+        int lt, mo = 0;  // tile of the XCD's run, activation row offset in it
         if (idx < 0) {
-            half = true;
+            part = 2;
             lt = R * P.W + hr / 2;
-            mh = hr & 1;
+            mo = 128 * (hr & 1);
             idx = 0;
         } else if (idx < R) {
             lt = idx * P.W + j;
@@ -351,10 +387,16 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
             lt = R * P.W + j;
             ++idx;
         } else if (hnext < H) {
-            half = true;
+            part = 2;
             lt = R * P.W + hnext / 2;
-            mh = hnext & 1;
+            mo = 128 * (hnext & 1);
             hnext += P.W;
+        } else if (quarter_left) {
+            part = 1;
+            const int h = H + hr / 2;  // the half tile this quarter belongs to
+            lt = R * P.W + h / 2;
+            mo = 128 * (h & 1) + 64 * (hr & 1);
+            quarter_left = false;
         } else {
             break;
         }
@@ -372,7 +414,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
         n0 = n0 < N - 256 ? n0 : N - 256;
         int Ng;
         const int g = group_of(G, n0, Ng);
-        if (!half) {
+        if (part == 4) {
             m0 = m0 < mp - 256 ? m0 : mp - 256;
             const PipeOffsets po = pipe_offsets<4>(tid, wn, wm, lane);
             v16f acc[4][4];
@@ -380,14 +422,23 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
                                   tile_rsrc(A + (size_t)m0 * K, 256u * (uint32_t)K), voff, step, K / kBK, po);
             store_acc<4>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
                          act_dq * G.w_scale[g]);
-        } else {
-            m0 += 128 * mh;
+        } else if (part == 2) {
+            m0 += mo;
             m0 = m0 < mp - 128 ? m0 : mp - 128;
             const PipeOffsets po = pipe_offsets<2>(tid, wn, wm, lane);
             v16f acc[4][2];
             tile_mainloop<2, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
                                   tile_rsrc(A + (size_t)m0 * K, 128u * (uint32_t)K), voff, step, K / kBK, po);
             store_acc<2>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
+                         act_dq * G.w_scale[g]);
+        } else {
+            m0 += mo;
+            m0 = m0 < mp - 64 ? m0 : mp - 64;
+            const PipeOffsets po = pipe_offsets<1>(tid, wn, wm, lane);
+            v16f acc[4][1];
+            tile_mainloop<1, F16>(acc, smem, tile_rsrc(G.w[g] + (size_t)n0 * K, 256u * (uint32_t)K),
+                                  tile_rsrc(A + (size_t)m0 * K, 64u * (uint32_t)K), voff, step, K / kBK, po);
+            store_acc<1>(acc, tile_out_rsrc(G.y[g], M, Ng, m0), (uint32_t)Ng, (uint32_t)n0, wn, wm, lane,
                          act_dq * G.w_scale[g]);
         }
     }

@@ -321,9 +321,11 @@ def _interior_items(T, W):
     kernel builds them: XCD x (workgroups w with w % 8 == x, j = w // 8)
     takes a contiguous run of Tx tiles; R = Tx // W whole rounds (tile
     r*W + j), the L left over as 2L half tiles when R > 0 or 2L <= W (else
-    whole, one per workgroup j < L); halves handed out odd workgroups first,
-    an odd one running its first half before its whole tiles.
-    -> {(x, j): [("w", tile) | ("h", tile, half)]}"""
+    whole, one per workgroup j < L); when W < 2L <= 1.5 W the halves beyond
+    the first W are split into quarters, one per workgroup; halves and
+    quarters handed out odd workgroups first, an odd one running its first
+    half before its whole tiles.
+    -> {(x, j): [("w", tile) | ("h", tile, half) | ("q", tile, half, quarter)]}"""
     out = {}
     tall, trem = divmod(T, 8)
     for x in range(8):
@@ -332,6 +334,9 @@ def _interior_items(T, W):
         r, l = divmod(tx, W)
         halves = r > 0 or 2 * l <= W
         h = 2 * l if halves else 0
+        nq = 0
+        if h > W and 2 * (h - W) <= W:
+            nq, h = 2 * (h - W), W
         for j in range(W):
             hr = j // 2 if j % 2 else W // 2 + j // 2
             items = []
@@ -343,6 +348,9 @@ def _interior_items(T, W):
                 items.append(("w", first + r * W + j))
             for q in range(hr + (W if early else 0), h, W):
                 items.append(("h", first + r * W + q // 2, q % 2))
+            if hr < nq:
+                hh = h + hr // 2
+                items.append(("q", first + r * W + hh // 2, hh % 2, hr % 2))
             out[(x, j)] = items
     return out
 
@@ -363,15 +371,27 @@ def test_interior_schedule_covers_tiles_once(tiles_m, tiles_n, W):
     seen = {}
     for lst in items.values():
         for it in lst:
-            key = (it[1], it[2]) if it[0] == "h" else (it[1], None)
+            key = (it[1],) + tuple(it[2:])
             seen[key] = seen.get(key, 0) + 1
     assert all(v == 1 for v in seen.values())
-    for t in range(T):  # whole, or both halves
-        assert ((t, None) in seen) != ((t, 0) in seen and (t, 1) in seen)
-        assert ((t, 0) in seen) == ((t, 1) in seen)
-    # load in half-tile units: at most one tile above the average
-    load = {wj: sum(2 if it[0] == "w" else 1 for it in lst) for wj, lst in items.items()}
-    assert max(load.values()) <= -(-2 * T // (8 * W)) + 2
+    for t in range(T):  # whole, or both halves, each half whole or as its two quarters
+        halves = [((t, hf) in seen) + ((t, hf, 0) in seen and (t, hf, 1) in seen) for hf in (0, 1)]
+        assert ((t,) in seen) != (halves == [1, 1])
+        assert halves in ([0, 0], [1, 1])
+        for hf in (0, 1):
+            assert ((t, hf, 0) in seen) == ((t, hf, 1) in seen)
+            assert not ((t, hf) in seen and (t, hf, 0) in seen)
+    # load in quarter-tile units: at most one tile above the average
+    size = {"w": 4, "h": 2, "q": 1}
+    load = {wj: sum(size[it[0]] for it in lst) for wj, lst in items.items()}
+    assert max(load.values()) <= -(-4 * T // (8 * W)) + 4
+    # no workgroup runs two halves where quarters can take the excess
+    tall, trem = divmod(T, 8)
+    for (x, j), lst in items.items():
+        tx = tall + (1 if x < trem else 0)
+        r, l = divmod(tx, W)
+        if r > 0 and 2 * l <= W + W // 2:
+            assert sum(it[0] == "h" for it in lst) <= 1 and sum(it[0] == "q" for it in lst) <= 1
     # with whole rounds and half tiles, every odd workgroup that has a half runs it first
     for (x, j), lst in items.items():
         if j % 2 and any(it[0] == "h" for it in lst) and any(it[0] == "w" for it in lst):

@@ -382,6 +382,10 @@ def _codes(g, shape):
     (2000, 18900, 512, False),   # ragged M and N: 2 rounds + halves, last tile at (1744, 18644)
     (768, 25700, 512, False),    # 303 tiles, one round + halves, the last n-tile at 25444
     (1000, 40000, 512, False),   # 2 rounds + halves, ragged M and N
+    # 52 tiles per XCD: one round, the 20 left over as 32 halves + 16 quarters
+    (2048, 13312, 512, True),
+    (2000, 13300, 512, False),   # ragged M and N: the last m-tile at 1744, its quarters up to 1936
+    (1000, 26624, 512, False),   # 4 m-tiles, the last at 752: quarters clamped to end at 1008
 ])
 def test_gemm_interior_plans(rz, m, n, k, full):
     mp = fp8_path.pad_m(m)
@@ -572,7 +576,7 @@ def test_gemm_split_on_two_streams(rz):
 
 
 @pytest.mark.parametrize("m,k,ns", [
-    (2048, 1024, (18944, 18944)),    # gate/up widths: one launch of 1184 tiles (all whole)
+    (2048, 1024, (18944, 18944)),    # gate/up widths: one launch of 1184 tiles (4 rounds, halves, quarters)
     (4096, 512, (3584, 512, 512)),   # q/k/v widths at M=4096: 288 tiles, one round + half tiles
     (2000, 512, (2560, 1024, 256)),  # ragged M, groups of 10, 4 and 1 n-tiles
     (4096, 512, (1024, 0, 512, 2048)),  # a skipped (zero-width) GEMM
