@@ -15,8 +15,17 @@ value = GEMM FLOPs of the step (3 x 2*M*N*K) / measured step time, TFLOP/s.
 roofline = the gate+up GEMM launch (one rz_fp8_gemm_group call, 2 x 2*M*N*K
 per launch) timed with HIP events on its stream during the timed steps (the
 only markers in the timed loop, around that launch on every 4th step),
-against the 5.0 PFLOP/s dense FP8 peak.  phases_us comes from a second,
-untimed pass of the same steps with markers between all phases.
+against the 5.0 PFLOP/s dense FP8 peak.  roofline.clock = the GFX clock and
+board power read from the GPU's metrics (amdsmi, read only) during a 3.2 s
+untimed run of the same steps after the timed ones (the firmware refreshes
+those values once a second), and the gate+up rate against the FP8 peak
+scaled to that clock.  Before the
+warm-up steps the step runs
+untimed for --clock-settle seconds (0.15): from idle the GPU raises its
+clock over tens of milliseconds, and a few warm-up steps would time that
+ramp instead of the sustained rate.  phases_us comes
+from a second, untimed pass of the same steps with markers between all
+phases.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload (see
 --help).
 
@@ -47,6 +56,13 @@ accuracy on the gate GEMM.
 K-quant blocks inside the kernel (no FP8 weight cache) beside the cached
 path's GEMM, at the model's prefill shapes (warm).
 
+--gemm-clock instead runs the gate+up GEMM launch back to back for a few
+seconds each with random E4M3 codes, with constant codes (every product 1.0)
+and with random codes again, and reports per phase the launch time, the GFX
+clock and board power read from the GPU's metrics meanwhile (amdsmi, read
+only; the values change once a second): the clock the MFMA load leaves the
+kernel, and its rate at that clock.
+
 --hbm-rates instead times torch's own device kernels on 1 GiB (a max and a
 sum that only read, a copy, a fill that only writes), cold (after a 1 GiB
 write) and warm, and a 155 MB max right after a 310 MB write (the down
@@ -69,7 +85,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
-FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (at 2.4 GHz)
+CLOCK_PASS_S = 3.2  # seconds of the untimed clock pass (about 3 refreshes of the GPU's metrics)
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock.json")
@@ -121,6 +138,145 @@ def measured_clock(path=None, sources=None):
     return {"mhz": mhz, "mfma_busy_of_active": rec["mfma_busy_of_active"], "launch_us": rec["launch_us"],
             "tflops": rec["tflops"], "frac_at_clock": round(rec["tflops"] / (FP8_PEAK_TFLOPS * mhz / 2400.0), 4),
             "source": rec.get("source")}
+
+
+class GpuMetrics:
+    """GFX clock and board power read every ~5 ms by a thread of this process
+    (amdsmi, read only: the calls torch's own clock_rate and power_draw make
+    on ROCm) between start() and close().  The values themselves change once
+    a second (the firmware's refresh), so a window needs seconds to hold a
+    few of them."""
+
+    def __init__(self, device_index=0):
+        import threading
+        self.samples = []
+        self._thread = None
+        self.error = None
+        self.power_cap_w = None
+        self._stop = threading.Event()
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) != 1:
+                raise RuntimeError(f"{len(hs)} GPUs visible, cannot tell which one is measured")
+            self._h = hs[device_index]
+            self._smi = amdsmi
+            cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+            self.power_cap_w = cap / 1e6 if isinstance(cap, int) and cap > 0 else None
+        except Exception as e:  # no amdsmi, or no permission: no clock in the line
+            self.error = repr(e)
+        self._thread = None
+
+    def start(self):
+        import threading
+        if self.error is None and self._thread is None:
+            self._stop.clear()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def _run(self):
+        smi, h = self._smi, self._h
+        while not self._stop.is_set():
+            try:
+                mhz = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX).get("clk")
+                w = smi.amdsmi_get_power_info(h).get("current_socket_power")
+            except Exception as e:
+                self.error = repr(e)
+                return
+            self.samples.append((time.monotonic(), mhz if isinstance(mhz, (int, float)) and 0 < mhz < 10000 else None,
+                                 w if isinstance(w, (int, float)) and 0 < w < 10000 else None))
+            self._stop.wait(0.005)
+
+    def window(self, t0, t1):
+        """Mean clock and power over the samples taken in [t0, t1] (time.monotonic())."""
+        sel = [x for x in list(self.samples) if t0 <= x[0] <= t1]
+        mhz = [x[1] for x in sel if x[1]]
+        w = [x[2] for x in sel if x[2]]
+        if not mhz:
+            return {"error": self.error or "no samples in the window"}
+        readings = [x[1:] for i, x in enumerate(sel) if i == 0 or x[1:] != sel[i - 1][1:]]
+        return {"gfxclk_mhz": round(sum(mhz) / len(mhz), 1), "gfxclk_mhz_min": round(min(mhz), 1),
+                "socket_power_w": round(sum(w) / len(w), 1) if w else None, "power_cap_w": self.power_cap_w,
+                "samples": len(sel), "readings": len(readings),
+                "readings_mhz_w": [[r[0], r[1]] for r in readings[:8]],
+                "source": "amdsmi GFX clock and socket power, read every ~5 ms (the values change once a second)"}
+
+    def close(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=5)
+            self._thread = None
+
+
+def at_clock(tflops, sample, key="gfxclk_mhz"):
+    """The rate against the FP8 peak scaled from 2.4 GHz to the measured clock."""
+    if not sample or key not in sample:
+        return sample
+    out = dict(sample)
+    out["frac_at_clock"] = round(tflops / (FP8_PEAK_TFLOPS * sample[key] / 2400.0), 4)
+    return out
+
+
+def gemm_clock(args, dev, metrics) -> int:
+    """The gate+up launch back to back with random and with constant codes,
+    clock and power sampled meanwhile (one line)."""
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+
+    m, k, n = 2048, 3584, 18944
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator().manual_seed(20260)
+
+    def codes(shape):  # E4M3 codes except the NaN codes 0x7F / 0xFF
+        a = torch.randint(0, 0x7F, shape, generator=g, dtype=torch.int32)
+        sgn = torch.randint(0, 2, shape, generator=g, dtype=torch.int32) << 7
+        return (a | sgn).to(torch.uint8).to(dev)
+
+    if metrics is not None:
+        metrics.start()
+    a, w1, w2 = codes((m, k)), codes((n, k)), codes((n, k))
+    one_a = torch.full((m, k), 0x38, dtype=torch.uint8, device=dev)  # 1.0
+    one_w = torch.full((n, k), 0x38, dtype=torch.uint8, device=dev)
+    sc = torch.tensor([1.0, 0.013, 0, 0], dtype=torch.float32, device=dev)
+    ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
+    flop = 2.0 * m * 2 * n * k
+    rows = {}
+    for name, fn in (("random codes", lambda: rz.rz_fp8_gemm_group(a, m, sc, [(w1, 0.007), (w2, 0.008)], ys, stream)),
+                     ("constant codes", lambda: rz.rz_fp8_gemm_group(one_a, m, sc, [(one_w, 0.007), (one_w, 0.008)],
+                                                                    ys, stream)),
+                     ("random codes again", lambda: rz.rz_fp8_gemm_group(a, m, sc, [(w1, 0.007), (w2, 0.008)], ys,
+                                                                        stream))):
+        time.sleep(1.0)  # idle: the clock and power settle back
+        for _ in range(200):  # 50 ms: the clock reaches its steady state under the load
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.monotonic()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launches, busy_ms = 0, 0.0
+        while time.monotonic() - t0 < args.clock_seconds:
+            for _ in range(50):
+                fn()
+            launches += 50
+            e1.record(stream)
+            e1.synchronize()
+            busy_ms += e0.elapsed_time(e1)
+            e0.record(stream)
+        t1 = time.monotonic()
+        us = busy_ms * 1e3 / launches
+        tf = flop / (us * 1e-6) / 1e12
+        rows[name] = at_clock(tf, metrics.window(t0 + 0.3, t1) if metrics else None) or {}
+        rows[name].update({"launch_us": round(us, 1), "tflops": round(tf, 1), "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                           "launches": launches})
+        log(f"{name}: {rows[name]}")
+    print(json.dumps({"metric": "gate+up FP8 GEMM launch back to back: GFX clock, board power and rate",
+                      "unit": "TFLOP/s", "higher_is_better": True, "peak": FP8_PEAK_TFLOPS, "rows": rows,
+                      "data": "synthetic",
+                      "config": {"workload": "M=2048, N=2x18944, K=3584 in one rz_fp8_gemm_group launch; random E4M3 "
+                                             "codes (NaN codes excluded) or every code 0x38 (1.0)"}}), flush=True)
+    return 0
 
 
 def cpu_baseline(x_ffn, x_down, gate_blocks, down_blocks, gate, dn, m_rows=128):
@@ -695,6 +851,14 @@ def main() -> int:
                     help="instead time the FP16 cached-weight comparator beside the FP8 path (warm, M=2048 FFN)")
     ap.add_argument("--q8-gemm", action="store_true",
                     help="instead time the integer path (Q8_1 activation x Q4_K weight) beside the FP8 path (warm)")
+    ap.add_argument("--gemm-clock", action="store_true",
+                    help="instead run the gate+up GEMM back to back with random and constant codes, sampling the "
+                         "GFX clock and board power")
+    ap.add_argument("--clock-seconds", type=float, default=3.0, help="seconds per --gemm-clock phase")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock pass (the GPU's clock and power readings) after the timed steps")
+    ap.add_argument("--clock-settle", type=float, default=0.15,
+                    help="seconds of untimed steps before the warm-up steps (the GPU raising its clock from idle)")
     ap.add_argument("--hbm-rates", action="store_true",
                     help="time torch's read, copy and write kernels on 1 GiB instead (HBM rates on this GPU)")
     ap.add_argument("--kquant-gemm", action="store_true",
@@ -729,6 +893,27 @@ def main() -> int:
         del src, dst
     if args.hbm_rates:
         return hbm_rates(args, dev)
+    # board clock and power readings (refreshed once a second): the default
+    # step's clock pass and --gemm-clock
+    sampled = not any((args.pack_model, args.gemm_shapes, args.kquant_gemm, args.fp16_gemm, args.q8_gemm,
+                       args.small_m is not None)) and not args.no_clock
+    metrics = GpuMetrics() if sampled else None
+    try:
+        return measure(args, dev, metrics)
+    finally:
+        if metrics is not None:
+            metrics.close()
+
+
+def measure(args, dev, metrics) -> int:
+    import numpy as np
+    import torch
+
+    import fp8_prefill_gemm_amd as rz
+    import workloads as W
+
+    if args.gemm_clock:
+        return gemm_clock(args, dev, metrics)
     if args.pack_model:
         return pack_model(args, dev)
     if args.gemm_shapes:
@@ -809,7 +994,27 @@ def main() -> int:
         rz.rz_fp8_gemm(a8_down, w8["down"], M, sc_down, s_down, y["down"], stream, gws)
         mark(5)
 
-    log(f"warmup {args.warmup} steps")
+    # everything the timed pass needs is made before the GPU starts working:
+    # the markers, and no garbage collection from here on (a full collection
+    # over the interpreter's objects stalls the host for milliseconds, the
+    # GPU idles meanwhile and lowers its clock; and the host issues every
+    # launch of the next phase after the pack's scale readback)
+    every = 4
+    gev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, args.steps, every)}
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    gc.collect()
+    gc.disable()
+    # clock settle: from idle the GPU raises its clock over tens of
+    # milliseconds (measured: gate+up launch 0.38 of peak after 3 steps, 0.43
+    # after 10, 0.45-0.46 from 100 on), so the step runs untimed for a fixed
+    # time before the warm-up steps, whatever their number
+    c0 = time.monotonic()
+    settle_steps = 0
+    while time.monotonic() - c0 < args.clock_settle:
+        step()
+        settle_steps += 1
+    torch.cuda.synchronize()
+    log(f"clock settle: {settle_steps} steps in {time.monotonic() - c0:.3f} s; warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -817,28 +1022,36 @@ def main() -> int:
     # timed pass: the only markers are the two around the gate+up GEMM
     # launch, on every 4th step (each marker leaves a 3-6 us gap between
     # kernels, so markers on every step would add ~9 us to each)
-    every = 4
-    gev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, args.steps, every)}
-    log(f"timing {args.steps} steps")
-    # no garbage collection inside the timed loop: a full collection over the
-    # interpreter's objects stalls the host for milliseconds, and the host
-    # issues every launch of the next phase after the pack's scale readback
-    gc.collect()
-    gc.disable()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(gemm_events=gev.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gc.enable()
+    log(f"timed {args.steps} steps")
+    # clock pass (untimed): the GFX clock and board power under the same
+    # steps, read from the GPU's metrics; the firmware refreshes them once a
+    # second, so the pass runs for CLOCK_PASS_S seconds and keeps the
+    # readings after its first 0.5 s
+    clock = None
+    if metrics is not None:
+        metrics.start()
+        r0 = time.monotonic()
+        clock_steps = 0
+        while time.monotonic() - r0 < CLOCK_PASS_S:
+            step()
+            clock_steps += 1
+        torch.cuda.synchronize()
+        clock = metrics.window(r0 + 0.5, time.monotonic())
+        metrics.close()
+        clock["window"] = f"{clock_steps} untimed steps ({CLOCK_PASS_S} s) after the timed ones, from 0.5 s on"
+        log(f"clock pass: {clock}")
     gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev.values()])) * 1e3
 
     # diagnostic pass (not timed as a whole): markers between every phase
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(events=ev[i])
     torch.cuda.synchronize()
+    gc.enable()
 
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     ph = {p: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3 for i, p in enumerate(phases)}
@@ -875,6 +1088,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "clock_settle": {"seconds": args.clock_settle, "steps": settle_steps},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -894,10 +1108,11 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
-            # the counter run's clock: its launch ran alone (counter
-            # collection serialises dispatches), so at a higher clock than
-            # the back-to-back timed pass
-            "clock": measured_clock(),
+            # GFX clock and board power over the timed steps
+            "clock": at_clock(achieved, clock),
+            # the counter run (GRBM_GUI_ACTIVE, MFMA busy cycles): its launch
+            # ran alone (counter collection serialises dispatches)
+            "mfma_counters": measured_clock(),
         },
         "phases_us": {k: round(v, 2) for k, v in ph.items()},
         "hbm_phases": hbm,
