@@ -16,9 +16,10 @@ roofline = the gate+up GEMM launch (one rz_fp8_gemm_group call, 2 x 2*M*N*K
 per launch) timed with HIP events on its stream during the timed steps (the
 only markers in the timed loop, around that launch on every 4th step),
 against the 5.0 PFLOP/s dense FP8 peak.  roofline.clock = the GFX clock and
-board power read from the GPU's metrics (amdsmi, read only) during a 3.2 s
+board power read from the GPU's metrics (amdsmi, read only) during a 3.5 s
 untimed run of the same steps after the timed ones (the firmware refreshes
-those values once a second), and the gate+up rate against the FP8 peak
+those values once a second; the readings from 1.05 s on), and the gate+up
+rate against the FP8 peak
 scaled to that clock.  Before the
 warm-up steps the step runs
 untimed for --clock-settle seconds (0.15): from idle the GPU raises its
@@ -86,7 +87,7 @@ if ROOT not in sys.path:
 
 METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (at 2.4 GHz)
-CLOCK_PASS_S = 3.2  # seconds of the untimed clock pass (about 3 refreshes of the GPU's metrics)
+CLOCK_PASS_S = 3.5  # seconds of the untimed clock pass (2-3 refreshes of the GPU's metrics after its first second)
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock.json")
@@ -1031,7 +1032,8 @@ def measure(args, dev, metrics) -> int:
     # clock pass (untimed): the GFX clock and board power under the same
     # steps, read from the GPU's metrics; the firmware refreshes them once a
     # second, so the pass runs for CLOCK_PASS_S seconds and keeps the
-    # readings after its first 0.5 s
+    # readings from 1.05 s on (a value read earlier may have been refreshed
+    # before the pass, during the setup's idle time)
     clock = None
     if metrics is not None:
         metrics.start()
@@ -1041,9 +1043,9 @@ def measure(args, dev, metrics) -> int:
             step()
             clock_steps += 1
         torch.cuda.synchronize()
-        clock = metrics.window(r0 + 0.5, time.monotonic())
+        clock = metrics.window(r0 + 1.05, time.monotonic())
         metrics.close()
-        clock["window"] = f"{clock_steps} untimed steps ({CLOCK_PASS_S} s) after the timed ones, from 0.5 s on"
+        clock["window"] = f"{clock_steps} untimed steps ({CLOCK_PASS_S} s) after the timed ones, from 1.05 s on"
         log(f"clock pass: {clock}")
     gateup_events_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev.values()])) * 1e3
 
