@@ -133,6 +133,18 @@ def test_gemm_plans(rz, m, n, k):
     check_gemm(y, a, w, m, rows)
 
 
+@pytest.mark.parametrize("m,n", [(2048, 13312), (2000, 13300)])
+def test_gemm_quarter_tiles(rz, m, n):
+    # 52 tiles per XCD: one round of 32, the 20 left over as 32 half and 16
+    # quarter tiles (the fp16 instance of the interior kernel); every row
+    # checked, ragged M and N in the second case
+    k = 256
+    a, w = _operands(2600 + m, m, n, k)
+    print(f"\n  fp16 gemm quarter tiles m={m} n={n} k={k}", flush=True)
+    y = host(rz.rz_fp16_gemm(dev(a), dev(w), m))
+    check_gemm(y, a, w, m)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
 def test_configs_from_blocks(rz, cfg):
     # the whole comparator path from the K-quant blocks, every output row
