@@ -8,25 +8,24 @@ weights, K=3584):
 One step is one pass of the whole path over that batch: pack the three
 weights (dequantise, absmax, E4M3 encode) in one call with one host wait for
 their scales, quantise the FFN input once for gate and up, run gate and up
-(one grouped launch), quantise the down input, run down.  Inputs are synthetic (seeded), resident in
-HBM before timing.
+(one grouped launch), quantise the down input, run down.  Inputs are
+synthetic (seeded), resident in HBM before timing.
 
 value = GEMM FLOPs of the step (3 x 2*M*N*K) / measured step time, TFLOP/s.
 roofline = the gate+up GEMM launch (one rz_fp8_gemm_group call, 2 x 2*M*N*K
 per launch) timed with HIP events on its stream during the timed steps (the
 only markers in the timed loop, around that launch on every 4th step),
-against the 5.0 PFLOP/s dense FP8 peak.  roofline.clock = the GFX clock and
+against the 5.0 PFLOP/s dense FP8 peak; traffic and mfma_counters come from
+the committed counter runs of the same kernel (profiles/, null once the
+kernel's sources differ from the ones measured); clock = the GFX clock and
 board power read from the GPU's metrics (amdsmi, read only) during a 3.5 s
 untimed run of the same steps after the timed ones (the firmware refreshes
 those values once a second; the readings from 1.05 s on), and the gate+up
-rate against the FP8 peak
-scaled to that clock.  Before the
-warm-up steps the step runs
-untimed for --clock-settle seconds (0.15): from idle the GPU raises its
-clock over tens of milliseconds, and a few warm-up steps would time that
-ramp instead of the sustained rate.  phases_us comes
-from a second, untimed pass of the same steps with markers between all
-phases.
+rate against the FP8 peak scaled to that clock.  Before the warm-up steps
+the step runs untimed for --clock-settle seconds (0.15): from idle the GPU
+raises its clock over tens of milliseconds, and a few warm-up steps would
+time that ramp instead of the sustained rate.  phases_us comes from a
+second, untimed pass of the same steps with markers between all phases.
 cpu_baseline = the CPU oracle on a bounded sample of the same workload (see
 --help).
 
