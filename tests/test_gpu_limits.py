@@ -1,5 +1,6 @@
 """GPU tests at the boundary's size limits: the largest K the GEMM accepts
-on each plan that small M takes, and an activation quantisation and a weight
+on each plan that small M takes, the interior kernel with more than 2^32
+outputs or activation bytes, and an activation quantisation and a weight
 pack of more than 2^32 elements (element indices past 32 bits).  The inputs
 are built so that the oracle checks them on a few distinct values or rows:
 all-1.0 codes make every partial sum of the GEMM an integer below 2^24
@@ -39,6 +40,22 @@ def test_gemm_largest_k(rz, m, n):
     torch.cuda.synchronize()
     assert tuple(y.shape) == (m, n)
     assert bool((y == float(k)).all()), f"{int((y != float(k)).sum())} outputs differ from {k}"
+    del a8, w8, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m,n,k", [(65536, 65536, 512),    # 2^32 outputs (17 GB): 65536 interior tiles
+                                   (300000, 256, 16384)])  # a 4.9 GB activation, 1172 m-tiles
+def test_gemm_interior_past_2_32(rz, m, n, k):
+    mp = rz.rz_pad_m(m)
+    assert rz.rz_fp8_gemm_plan(m, n, k)[:2] == (256, 256)
+    print(f"interior gemm m={m} n={n} k={k}", flush=True)
+    a8 = torch.full((mp, k), 0x38, dtype=torch.uint8, device="cuda")
+    w8 = torch.full((n, k), 0x38, dtype=torch.uint8, device="cuda")
+    sc = torch.tensor([1.0, 1.0, 0.0, 0.0], dtype=torch.float32, device="cuda")
+    y = rz.rz_fp8_gemm(a8, w8, m, sc, 0.5)
+    torch.cuda.synchronize()
+    assert bool((y == float(k) * 0.5).all())
     del a8, w8, y
     torch.cuda.empty_cache()
 
