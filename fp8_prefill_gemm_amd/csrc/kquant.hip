@@ -173,33 +173,40 @@ __device__ __forceinline__ void encode_part(const uint8_t* __restrict__ blocks, 
                                             uint8_t* __restrict__ w_fp8, float q, bool tensor_finite) {
     if constexpr (QT == 12) {
         visit_units<12, kEncodeUnits>(blocks, nb, bid, ngroups, [&](uint64_t b, int s, uint4 head, uint4 qs) {
-            Q4Unit u;
-            q4k_decode_unit(head, qs, s, u);
+            // each run of 16 encoded as soon as it is decoded (fewer live
+            // registers, more waves per SIMD to overlap memory with the ALU)
             uint8_t* o = w_fp8 + b * kQK + 64 * (s >> 1) + 16 * (s & 1);
             const bool fast = tensor_finite && half_finite(head.x) && half_finite(head.x >> 16);
+            float v[16];
             if (__all(fast)) {
-                *reinterpret_cast<uint4*>(o) = e4m3_scaled16<true>(u.lo, q);
-                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16<true>(u.hi, q);
+                q4k_decode_run<false>(head, qs, s, v);
+                *reinterpret_cast<uint4*>(o) = e4m3_scaled16<true>(v, q);
+                q4k_decode_run<true>(head, qs, s, v);
+                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16<true>(v, q);
             } else {
-                *reinterpret_cast<uint4*>(o) = e4m3_scaled16(u.lo, q);
-                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16(u.hi, q);
+                q4k_decode_run<false>(head, qs, s, v);
+                *reinterpret_cast<uint4*>(o) = e4m3_scaled16(v, q);
+                q4k_decode_run<true>(head, qs, s, v);
+                *reinterpret_cast<uint4*>(o + 32) = e4m3_scaled16(v, q);
             }
         });
     } else {
         visit_units<14, kEncodeUnits / 2>(blocks, nb, bid, ngroups,
                         [&](uint64_t b, int h, int l0, uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits) {
-                            Q6Unit u;
                             uint8_t* o = w_fp8 + b * kQK + 128 * h + l0;
+                            float v[16];  // one run of 16 at a time
                             if (__all(tensor_finite && half_finite(dbits))) {
-                                q6k_decode_unit<true>(ql_a, ql_b, qh, sc4, dbits, u);
 #pragma unroll
-                                for (int p = 0; p < 4; ++p)
-                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16<true>(u.v[p], q);
+                                for (int p = 0; p < 4; ++p) {
+                                    q6k_decode_run<true>(ql_a, ql_b, qh, sc4, dbits, p, v);
+                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16<true>(v, q);
+                                }
                             } else {
-                                q6k_decode_unit(ql_a, ql_b, qh, sc4, dbits, u);
 #pragma unroll
-                                for (int p = 0; p < 4; ++p)
-                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16(u.v[p], q);
+                                for (int p = 0; p < 4; ++p) {
+                                    q6k_decode_run(ql_a, ql_b, qh, sc4, dbits, p, v);
+                                    *reinterpret_cast<uint4*>(o + 32 * p) = e4m3_scaled16(v, q);
+                                }
                             }
                         });
     }

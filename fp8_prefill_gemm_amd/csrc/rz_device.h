@@ -228,6 +228,25 @@ __device__ __forceinline__ void q4k_decode_unit(uint4 head, uint4 qs, int s, Q4U
     }
 }
 
+// One run of q4k_decode_unit: u.lo (kHi false) or u.hi (kHi true) alone,
+// the same values (for callers that encode a run as soon as it is decoded).
+template <bool kHi>
+__device__ __forceinline__ void q4k_decode_run(uint4 head, uint4 qs, int s, float (&v)[16]) {
+    const float d = half_bits_to_float(head.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(head.x >> 16);
+    uint32_t sc, mn;
+    q4k_scale_min(head, 2 * (s >> 1) + (kHi ? 1 : 0), sc, mn);
+    const float d0 = d * (float)sc, o0 = dmin * (float)mn;
+    const uint32_t w[4] = {qs.x, qs.y, qs.z, qs.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x = kHi ? (w[i] >> 4) & 0x0F0F0F0Fu : w[i] & 0x0F0F0F0Fu;
+        asm("" : "+v"(x));  // byte b converts with v_cvt_f32_ubyte<b>
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v[4 * i + b] = __builtin_fmaf(d0, (float)((x >> (8 * b)) & 0xFFu), -o0);
+    }
+}
+
 // Running per-byte maximum and minimum of the four bytes of w (each < 256)
 // with packed 16-bit integer max/min: bytes 0 and 2 go to the two 16-bit
 // halves of one operand, bytes 1 and 3 to the other.
@@ -310,6 +329,29 @@ __device__ __forceinline__ void q6k_decode_unit(uint4 ql_a, uint4 ql_b, uint4 qh
                 const float qf = (float)((q[p] >> (8 * b)) & 0xFFu);
                 u.v[p][4 * i + b] = kFinite ? __builtin_fmaf(ds[p], qf, -32.0f * ds[p]) : ds[p] * (qf - 32.0f);
             }
+    }
+}
+
+// Run p of q6k_decode_unit alone (u.v[p]), the same values.
+template <bool kFinite = false>
+__device__ __forceinline__ void q6k_decode_run(uint4 ql_a, uint4 ql_b, uint4 qh, uint32_t sc4, uint32_t dbits, int p,
+                                               float (&v)[16]) {
+    const float d = half_bits_to_float(dbits);
+    const float ds = d * (float)(int8_t)((sc4 >> (8 * p)) & 0xFFu);
+    const uint32_t A[4] = {ql_a.x, ql_a.y, ql_a.z, ql_a.w};
+    const uint32_t B[4] = {ql_b.x, ql_b.y, ql_b.z, ql_b.w};
+    const uint32_t H[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (p & 1) ? B[i] : A[i];
+        uint32_t q = ((p & 2) ? (lo >> 4) : lo) & 0x0F0F0F0Fu;
+        q |= ((H[i] >> (2 * p)) & 0x03030303u) << 4;
+        asm("" : "+v"(q));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float qf = (float)((q >> (8 * b)) & 0xFFu);
+            v[4 * i + b] = kFinite ? __builtin_fmaf(ds, qf, -32.0f * ds) : ds * (qf - 32.0f);
+        }
     }
 }
 
