@@ -86,6 +86,11 @@ if ROOT not in sys.path:
 
 METRIC = "FP8 prefill GEMM TFLOP/s & % FP8 MFMA peak (Q4_K w, M=2048, K=3584)"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (at 2.4 GHz)
+# per-shape modes: the mean over TIMED_LAUNCHES launches back to back between
+# two events (markers between launches would add their own gaps), after
+# WARM_LAUNCHES untimed ones; the kernel traces of the same runs give the
+# per-launch medians
+WARM_LAUNCHES, TIMED_LAUNCHES = 10, 50
 CLOCK_PASS_S = 3.5  # seconds of the untimed clock pass (2-3 refreshes of the GPU's metrics after its first second)
 HBM_PEAK_TBPS = 8.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
@@ -521,7 +526,7 @@ def small_m(args, dev) -> int:
 def gemm_shapes(args, dev) -> int:
     """Warm FP8 GEMM time per shape of the five configurations (one line):
     random E4M3 codes (no NaN codes), scales 1, the library's default
-    workspace, HIP events around 20 launches after 5 warm-up launches.  Also
+    workspace, HIP events around 50 launches after 10 warm-up launches.  Also
     the 28-layer sweep at M=4096 (7 GEMMs per layer, 53.46 TFLOP) from the
     per-shape times."""
     import torch
@@ -549,15 +554,15 @@ def gemm_shapes(args, dev) -> int:
         a = codes(rz.rz_pad_m(m), k)
         w = codes(n, k)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        for _ in range(5):
+        for _ in range(WARM_LAUNCHES):
             rz.rz_fp8_gemm(a, w, m, sc, 1.0, y, stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(20):
+        for _ in range(TIMED_LAUNCHES):
             rz.rz_fp8_gemm(a, w, m, sc, 1.0, y, stream)
         e1.record(stream)
         e1.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 20
+        t = e0.elapsed_time(e1) * 1e-3 / TIMED_LAUNCHES
         plan = rz.rz_fp8_gemm_plan(m, n, k)
         byts = n * k + rz.rz_pad_m(m) * k + 4 * m * n
         rows[name] = {"m": m, "n": n, "k": k, "us": round(t * 1e6, 2),
@@ -572,15 +577,15 @@ def gemm_shapes(args, dev) -> int:
         a = codes(rz.rz_pad_m(m), k)
         ws_ = [(codes(n, k), 1.0) for n in ns]
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for n in ns]
-        for _ in range(5):
+        for _ in range(WARM_LAUNCHES):
             rz.rz_fp8_gemm_group(a, m, sc, ws_, ys, stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(20):
+        for _ in range(TIMED_LAUNCHES):
             rz.rz_fp8_gemm_group(a, m, sc, ws_, ys, stream)
         e1.record(stream)
         e1.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 20
+        t = e0.elapsed_time(e1) * 1e-3 / TIMED_LAUNCHES
         plan = rz.rz_fp8_gemm_plan(m, sum(ns), k)
         rows[name] = {"m": m, "n": list(ns), "k": k, "us": round(t * 1e6, 2),
                       "tflops": round(2.0 * m * sum(ns) * k / t / 1e12, 1),
@@ -609,7 +614,7 @@ def kquant_gemm(args, dev) -> int:
     blocks in the kernel (rz_kquant_fp8_gemm), beside the cached path's GEMM
     on the packed weight (rz_fp8_gemm), per prefill shape of the 7B-class
     model (one line): seeded K-quant blocks and activations, HIP events
-    around 20 launches after 5 warm-up launches.  Also the one-pass weight
+    around 50 launches after 10 warm-up launches.  Also the one-pass weight
     scale (rz_kquant_weight_scale, including its host wait) and the weight
     bytes each path keeps resident for the 28-layer model."""
     import torch
@@ -624,8 +629,8 @@ def kquant_gemm(args, dev) -> int:
               ("cfg4 down", 4096, W.Q6_K, H, F)]
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn, reps=20):
-        for _ in range(5):
+    def timed(fn, reps=TIMED_LAUNCHES):
+        for _ in range(WARM_LAUNCHES):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -675,8 +680,8 @@ def kquant_gemm(args, dev) -> int:
 def fp16_gemm(args, dev) -> int:
     """The FP16 comparator (cached fp16 weight, fp16 activation, fp16 MFMA
     GEMM with fp32 accumulation) beside the FP8 path on the FFN shapes at
-    M=2048 (one line): warm GEMM times (HIP events around 20 launches after
-    5 warm-up launches), the one-off weight conversion and the per-input
+    M=2048 (one line): warm GEMM times (HIP events around 50 launches after
+    10 warm-up launches), the one-off weight conversion and the per-input
     activation conversion, the resident weight bytes, and the accuracy of
     both paths' gate outputs on 64 rows against a float64 product of the
     fp32 activation and the fp32 dequantised weight (computed here with
@@ -690,8 +695,8 @@ def fp16_gemm(args, dev) -> int:
     ffn, down = W.config_groups(3)
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn, reps=20):
-        for _ in range(5):
+    def timed(fn, reps=TIMED_LAUNCHES):
+        for _ in range(WARM_LAUNCHES):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -765,7 +770,7 @@ INT_PATH_ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * (32 / 3) * 2 / 1e12
 def q8_gemm(args, dev) -> int:
     """The integer path (Q8_1 activation x Q4_K weight) beside the FP8 path
     on the FFN gate/up shape at M=2048 and M=4096 and the attention Q shape
-    (one line): warm times, HIP events around 20 launches after 5 warm-up
+    (one line): warm times, HIP events around 50 launches after 10 warm-up
     launches, and the accuracy of both paths' outputs on 64 rows against a
     float64 product of the fp32 activation and the fp32 dequantised weight
     (torch float64 on the GPU, from rz_dequant_f32)."""
@@ -776,8 +781,8 @@ def q8_gemm(args, dev) -> int:
 
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn, reps=20):
-        for _ in range(5):
+    def timed(fn, reps=TIMED_LAUNCHES):
+        for _ in range(WARM_LAUNCHES):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
