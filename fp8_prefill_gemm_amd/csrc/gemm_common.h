@@ -41,9 +41,11 @@ __device__ __forceinline__ v16f mma32(const v8i& src0, const v8i& src1, v16f acc
 // bits 0 and 4 are the instruction's SC0 and SC1 scope bits.  Device scope
 // (SC1): a store writes through the XCD's L2 and completes once it is
 // visible to every XCD.  System scope (SC0 and SC1): a load misses in the
-// L1 and the L2 and reads memory.
+// L1 and the L2 and reads memory.  Bit 1 is NT, the streaming hint: the
+// line is not kept in the caches for reuse.
 constexpr int kScopeDevice = 16;
 constexpr int kScopeSystem = 17;
+constexpr int kNonTemporal = 2;
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
