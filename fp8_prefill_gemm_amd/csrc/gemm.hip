@@ -308,9 +308,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(float* Y, int M,
 //   activation rows instead, at most one per workgroup, so that no
 //   workgroup runs two halves (a half tile costs ~0.6 of a whole one).
 // Half and quarter tiles go out in half_rank order (the odd workgroups
-// first), and an odd workgroup runs its first half tile before its whole
-// tiles, an even one after them: the two halves of an XCD then reach the
-// end of their whole tiles half a tile apart.  Measured on the 256x256 tiles, the 256 KB
+// first), and an odd workgroup runs its quarter tile, or else its first
+// half tile, before its whole tiles, an even one after them: the two halves
+// of an XCD then reach the end of their whole tiles a quarter or half a tile
+// apart.  The two halves hold different activation rows but the same weight
+// rows; a quarter tile apart (~7 K-steps, under 3 MB of the XCD's loads)
+// the later half finds the weight rows still in the 4 MB L2, half a tile
+// apart it reads them again (gate+up at M=2048 in the FFN step: 242 against
+// 245 us).  Measured on the 256x256 tiles, the 256 KB
 // output store of a tile takes ~7k cycles when 16 CUs of an XCD store
 // together and ~16k when all 32 do, whether or not the other XCDs store at
 // the same time (the XCD's write path is the limit, not HBM).
@@ -370,16 +375,24 @@ __global__ __launch_bounds__(256) void fp8_gemm_interior_kernel(const uint8_t* _
         H = P.W;
     }
     const int hr = half_rank(j, P.W);
-    // items in order: [half hr if j is odd] [whole rounds] [the left-over
-    // whole tile j] [halves hr (j even), hr + W, hr + 2W, ...] [quarter hr]
-    const bool early = (j & 1) && hr < H;
-    int idx = early ? -1 : 0;  // -1: the early half; 0..R-1: rounds; R: left-over whole tile
+    // items in order: [quarter hr if j is odd, else half hr if j is odd]
+    // [whole rounds] [the left-over whole tile j] [halves hr (unless run
+    // early), hr + W, hr + 2W, ...] [quarter hr (unless run early)]
+    const bool early_q = (j & 1) && hr < Q;
+    const bool early = (j & 1) && hr < H && !early_q;
+    int idx = (early || early_q) ? -1 : 0;  // -1: the early quarter or half; 0..R-1: rounds; R: left-over whole tile
     int hnext = early ? hr + P.W : hr;
-    bool quarter_left = hr < Q;
+    bool quarter_left = hr < Q && !early_q;
     for (;;) {
         int part = 4;    // activation rows / 64: 4 whole, 2 half, 1 quarter
         int lt, mo = 0;  // tile of the XCD's run, activation row offset in it
-        if (idx < 0) {
+        if (idx < 0 && early_q) {
+            part = 1;
+            const int h = H + hr / 2;  // the half tile this quarter belongs to
+            lt = R * P.W + h / 2;
+            mo = 128 * (h & 1) + 64 * (hr & 1);
+            idx = 0;
+        } else if (idx < 0) {
             part = 2;
             lt = R * P.W + hr / 2;
             mo = 128 * (hr & 1);

@@ -323,8 +323,8 @@ def _interior_items(T, W):
     r*W + j), the L left over as 2L half tiles when R > 0 or 2L <= W (else
     whole, one per workgroup j < L); when W < 2L <= 1.5 W the halves beyond
     the first W are split into quarters, one per workgroup; halves and
-    quarters handed out odd workgroups first, an odd one running its first
-    half before its whole tiles.
+    quarters handed out odd workgroups first, an odd one running its
+    quarter, or else its first half, before its whole tiles.
     -> {(x, j): [("w", tile) | ("h", tile, half) | ("q", tile, half, quarter)]}"""
     out = {}
     tall, trem = divmod(T, 8)
@@ -340,7 +340,12 @@ def _interior_items(T, W):
         for j in range(W):
             hr = j // 2 if j % 2 else W // 2 + j // 2
             items = []
-            early = j % 2 == 1 and hr < h
+            hh = h + hr // 2
+            quarter = ("q", first + r * W + hh // 2, hh % 2, hr % 2) if hr < nq else None
+            early_q = j % 2 == 1 and quarter is not None
+            early = j % 2 == 1 and hr < h and not early_q
+            if early_q:
+                items.append(quarter)
             if early:
                 items.append(("h", first + r * W + hr // 2, hr % 2))
             items += [("w", first + i * W + j) for i in range(r)]
@@ -348,9 +353,8 @@ def _interior_items(T, W):
                 items.append(("w", first + r * W + j))
             for q in range(hr + (W if early else 0), h, W):
                 items.append(("h", first + r * W + q // 2, q % 2))
-            if hr < nq:
-                hh = h + hr // 2
-                items.append(("q", first + r * W + hh // 2, hh % 2, hr % 2))
+            if quarter is not None and not early_q:
+                items.append(quarter)
             out[(x, j)] = items
     return out
 
@@ -392,10 +396,14 @@ def test_interior_schedule_covers_tiles_once(tiles_m, tiles_n, W):
         r, l = divmod(tx, W)
         if r > 0 and 2 * l <= W + W // 2:
             assert sum(it[0] == "h" for it in lst) <= 1 and sum(it[0] == "q" for it in lst) <= 1
-    # with whole rounds and half tiles, every odd workgroup that has a half runs it first
+    # with whole rounds, every odd workgroup that has a quarter runs it first,
+    # else its first half
     for (x, j), lst in items.items():
-        if j % 2 and any(it[0] == "h" for it in lst) and any(it[0] == "w" for it in lst):
-            assert lst[0][0] == "h"
+        if j % 2 and any(it[0] == "w" for it in lst):
+            if any(it[0] == "q" for it in lst):
+                assert lst[0][0] == "q"
+            elif any(it[0] == "h" for it in lst):
+                assert lst[0][0] == "h"
 
 
 
