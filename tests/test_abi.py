@@ -359,6 +359,50 @@ def _interior_items(T, W):
     return out
 
 
+def _interior_group_m(tiles_m, tiles_n, W):
+    """Group height of the interior kernel's tile order, as its launch picks
+    it: 8 (or tiles_m if fewer); when an XCD's run fits one round, the height
+    of 4, 2, 1 below that which gives the run fewer distinct m- plus n-tiles."""
+    gm = min(tiles_m, 8)
+    tx = -(-tiles_m * tiles_n // 8)
+    if tx <= W:
+        cost = gm + -(-tx // gm)
+        for a in (4, 2, 1):
+            if a < gm and a + -(-tx // a) < cost:
+                gm, cost = a, a + -(-tx // a)
+    return gm
+
+
+def _grouped_origin(t, tiles_m, tiles_n, gm_full):
+    """(n-tile, m-tile) of tile t in the grouped order: groups of gm_full
+    m-tiles (the last may be shorter), m fastest inside a group."""
+    gidx, tin = divmod(t, gm_full * tiles_n)
+    first_m = gidx * gm_full
+    gm = min(tiles_m - first_m, gm_full)
+    return tin // gm, first_m + tin % gm
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,W,want", [(8, 14, 32, 4), (16, 14, 32, 4), (8, 148, 32, 8),
+                                                   (4, 18, 32, 4), (8, 74, 32, 8), (3, 100, 32, 3),
+                                                   (16, 148, 32, 8), (8, 14, 38, 4), (1, 64, 32, 1)])
+def test_interior_group_height(tiles_m, tiles_n, W, want):
+    gm = _interior_group_m(tiles_m, tiles_n, W)
+    assert gm == want
+    T = tiles_m * tiles_n
+    origins = [_grouped_origin(t, tiles_m, tiles_n, gm) for t in range(T)]
+    assert sorted(origins) == [(n, m) for n in range(tiles_n) for m in range(tiles_m)]
+    # distinct m- and n-tiles of each XCD's run: never more than with groups of 8
+    tall, trem = divmod(T, 8)
+    for x in range(8):
+        first = x * tall + min(x, trem)
+        run = range(first, first + tall + (1 if x < trem else 0))
+        def spread(g):
+            o = [_grouped_origin(t, tiles_m, tiles_n, g) for t in run]
+            return len({n for n, _ in o}) + len({m for _, m in o})
+        if -(-T // 8) <= W:
+            assert spread(gm) <= spread(min(tiles_m, 8)) + 1
+
+
 def test_interior_plan_examples(L):
     # the persistent interior kernel: one workgroup per CU (256 without a device)
     for m, n, k in [(2048, 18944, 3584), (2048, 3584, 18944), (4096, 18944, 3584), (768, 25600, 512),
