@@ -11,8 +11,9 @@
 // reduction is atomic-free: pass 1 writes one key per workgroup (wave
 // shuffles + LDS), one workgroup reduces those keys and publishes
 // {absmax, absmax'/448} for the GEMM and the encode scale 448/absmax', and
-// pass 2 (the encoder) reads that record: no zeroing, nothing left over
-// between calls.  HBM traffic: read x twice (4 + 4 bytes per element) and
+// pass 2 (the encoder) reads that record (for inputs with few keys every
+// encoder workgroup reduces them itself instead): no zeroing, nothing left
+// over between calls.  HBM traffic: read x twice (4 + 4 bytes per element) and
 // write 1 byte.
 #include <mutex>
 
@@ -88,11 +89,8 @@ __global__ __launch_bounds__(kThreads) void act_scales_kernel(const uint32_t* __
 // Pass 2 of the activation path.  count_real = m*k (a multiple of 256),
 // count_total = pad_m(m)*k; groups of 16 elements at or past count_real are
 // pad rows and are written as zero bytes.
-// rec: the {a, q, dq, 0} act_scales_kernel published.
-__global__ __launch_bounds__(kThreads) void act_encode_kernel(
-    const float* __restrict__ x, uint64_t count_real, uint64_t count_total,
-    const float* __restrict__ rec, uint8_t* __restrict__ out) {
-    const float q = rec[1];
+__device__ __forceinline__ void act_encode_body(const float* __restrict__ x, uint64_t count_real,
+                                                uint64_t count_total, float q, uint8_t* __restrict__ out) {
     const uint64_t groups = count_total >> 4;
     const uint64_t real_groups = count_real >> 4;
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
@@ -111,6 +109,31 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(
             o16[g] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
+}
+
+// rec: the {a, q, dq, 0} act_scales_kernel published.
+__global__ __launch_bounds__(kThreads) void act_encode_kernel(
+    const float* __restrict__ x, uint64_t count_real, uint64_t count_total,
+    const float* __restrict__ rec, uint8_t* __restrict__ out) {
+    act_encode_body(x, count_real, count_total, rec[1], out);
+}
+
+// The same pass for an input with at most kFusedPartials partial keys (up to
+// 32 MB of fp32): every workgroup reduces the keys itself (4 KB at most, one
+// load per thread, read from the L2 by all but the first workgroups) and
+// workgroup 0 publishes {a, dq} to act_scale, in place of act_scales_kernel:
+// one launch less for the same values.
+constexpr int kFusedPartials = 1024;
+__global__ __launch_bounds__(kThreads) void act_encode_reduce_kernel(
+    const float* __restrict__ x, uint64_t count_real, uint64_t count_total, const uint32_t* __restrict__ partial,
+    int npartial, float* __restrict__ act_scale, uint8_t* __restrict__ out) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const Scales sc = scales_from_key(reduce_partials<kThreads>(partial, npartial, red));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        act_scale[0] = sc.a;
+        act_scale[1] = sc.dq;
+    }
+    act_encode_body(x, count_real, count_total, sc.q, out);
 }
 
 // fp32 -> fp16 (to nearest even) of the activation for the FP16 comparator
@@ -198,8 +221,12 @@ hipError_t launch_quant_act(const float* x, uint64_t count_real, uint64_t count_
     const int g1 = absmax_groups(count_real);
     float* rec = reinterpret_cast<float*>(tail);
     absmax_partial_kernel<<<g1, kThreads, 0, st>>>(x, count_real, partial);
-    act_scales_kernel<<<1, kThreads, 0, st>>>(partial, g1, act_scale, rec);
     const int g2 = grid_for(count_total >> 4, 4096);
+    if (count_total && g1 <= kFusedPartials) {
+        act_encode_reduce_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, partial, g1, act_scale, a_fp8);
+        return hipGetLastError();
+    }
+    act_scales_kernel<<<1, kThreads, 0, st>>>(partial, g1, act_scale, rec);
     if (count_total) act_encode_kernel<<<g2, kThreads, 0, st>>>(x, count_real, count_total, rec, a_fp8);
     return hipGetLastError();
 }
